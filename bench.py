@@ -1,0 +1,203 @@
+"""Benchmark: one PixArt-style DiT block's linears in NVFP4 W4A4 on one MI355X.
+
+A step is the hot path for every linear of the block (qkv 1152->3456, proj 1152->1152,
+fc1 1152->4608, fc2 4608->1152 at M = 4096 tokens): dynamic NVFP4 quantization of the bf16
+activation (amax pass + quantize pass) followed by the W4A4 GEMM with bf16 output.  Weights are
+quantized and prepacked once before timing (offline, as a deployed model would ship them).
+Inputs are seeded synthetic tensors resident in device memory before the timed region.
+
+Prints one JSON line.  `value` is the block's GEMM work (sum of 2 M N K) divided by the measured
+step time, quantization included.  `roofline` describes the dominant GEMM launch, timed with HIP
+events on the stream the kernels run on.  `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload (a few hundred rows of every linear).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at DiT shapes; % of MFMA/HBM roofline"
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the NVFP4 hot path here is a single-device kernel set "
+              "(no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_quantized_gemm_amd as nv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- setup (untimed): inputs, offline weight prep, outputs, workspaces ----------------------
+    layers = []
+    for name, x, w in workloads.pixart():
+        M, K = x.shape
+        N = w.shape[0]
+        xd = x.to(dev)
+        wp, ws, wS = nv.nvfp4_quantize(w.to(dev))
+        bp = nv.nvfp4_prepack_weight(wp, ws)
+        del wp, ws
+        L = dict(name=name, M=M, N=N, K=K, x=xd, bp=bp, wS=wS,
+                 packed=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                 scales=torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                 S=torch.empty(1, dtype=torch.float32, device=dev),
+                 qws=torch.empty(nv.nvfp4_quantize_workspace_bytes(M, K), dtype=torch.uint8, device=dev),
+                 y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 gws=None, w_cpu=w, x_cpu=x)
+        need = nv.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K)
+        if need:
+            L["gws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    def run_layer(L, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_quantize(L["x"], L["S"], static=False, packed=L["packed"], scales=L["scales"],
+                          workspace=L["qws"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_gemm(nv.W4A4, L["packed"], L["scales"], L["S"], L["bp"], L["wS"], L["N"], L["K"],
+                      torch.bfloat16, out=L["y"], workspace=L["gws"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        for L in layers:
+            run_layer(L)
+    torch.cuda.synchronize()
+
+    # ---- timed region -------------------------------------------------------------------------------
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(args.steps):
+        for li, L in enumerate(layers):
+            run_layer(L, evs[s][li])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    flops_step = sum(2.0 * L["M"] * L["N"] * L["K"] for L in layers)
+    breakdown = {}
+    for li, L in enumerate(layers):
+        q_ms = sum(evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps)) / args.steps
+        g_ms = sum(evs[s][li][1].elapsed_time(evs[s][li][2]) for s in range(args.steps)) / args.steps
+        qbytes = L["M"] * L["K"] * (2 + 2 + 0.5625)  # amax read + quantize read + codes/scales write
+        flops = 2.0 * L["M"] * L["N"] * L["K"]
+        breakdown[L["name"]] = dict(
+            M=L["M"], N=L["N"], K=L["K"],
+            quantize_us=round(q_ms * 1e3, 2), quantize_GBps=round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            gemm_us=round(g_ms * 1e3, 2), gemm_TFLOPs=round(flops / (g_ms * 1e-3) / 1e12, 1),
+            gemm_frac=round(flops / (g_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4))
+    dom = max(breakdown.items(), key=lambda kv: kv[1]["gemm_us"])
+    dom_name, d = dom
+    roofline = dict(bound="mfma", achieved=d["gemm_TFLOPs"], peak=PEAK_FP16_TFLOPS, unit="TFLOP/s",
+                    frac=round(d["gemm_TFLOPs"] / PEAK_FP16_TFLOPS, 4), traffic=None,
+                    kernel=f"W4A4 GEMM {dom_name} M={d['M']} N={d['N']} K={d['K']}",
+                    algorithmic_flops_per_launch=2 * d["M"] * d["N"] * d["K"])
+    q_total_bytes = sum(L["M"] * L["K"] * 4.5625 for L in layers)
+    q_total_us = sum(v["quantize_us"] for v in breakdown.values())
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "PixArt-style DiT block linears, W4A4, bf16 in/out", "M": 4096, "hidden": 1152,
+                   "linears": {L["name"]: [L["K"], L["N"]] for L in layers}, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "quantize": {"achieved_GBps": round(q_total_bytes / (q_total_us * 1e-6) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
+                     "frac": round(q_total_bytes / (q_total_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "bytes_per_elem": 4.5625, "note": "dynamic: amax pass + quantize pass"},
+        "breakdown": breakdown,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, rows):
+    """CPU oracle on a bounded sample: per linear, the dynamic tensor scale over the full activation,
+    then quantize + dequantize + fp64-accumulated GEMM for `rows` rows against the full weight
+    (the weight's own quantization is offline on both sides and not timed)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.default_threads()
+    prep = []
+    for L in layers:
+        w16 = L["w_cpu"].view(torch.int16).numpy().view(np.uint16)
+        bp, bs, bS = oracle.quantize(w16, threads=threads)
+        B, _ = oracle.dequantize(bp, bs, bS, threads=threads)
+        x16 = L["x_cpu"].view(torch.int16).numpy().view(np.uint16)
+        prep.append((x16, B))
+    if rows <= 0:
+        # calibrate: aim for roughly 15 s of oracle work in total
+        x16, B = prep[0]
+        t = time.perf_counter()
+        S = oracle.tensor_scale(x16)
+        p, s, _ = oracle.quantize(np.ascontiguousarray(x16[:32]), S=S, threads=threads)
+        A, _ = oracle.dequantize(p, s, S, threads=threads)
+        oracle.gemm(A, B, threads=threads)
+        dt = time.perf_counter() - t
+        f0 = 2.0 * 32 * B.shape[0] * B.shape[1]
+        rate = f0 / max(dt, 1e-6)
+        total_per_row = sum(2.0 * Bx.shape[0] * Bx.shape[1] for _, Bx in prep)
+        rows = int(max(16, min(4096, 15.0 * rate / total_per_row)))
+    flops = 0.0
+    t = time.perf_counter()
+    for x16, B in prep:
+        S = oracle.tensor_scale(x16)
+        p, s, _ = oracle.quantize(np.ascontiguousarray(x16[:rows]), S=S, threads=threads)
+        A, _ = oracle.dequantize(p, s, S, threads=threads)
+        oracle.gemm(A, B, threads=threads)
+        flops += 2.0 * rows * B.shape[0] * B.shape[1]
+    dt = time.perf_counter() - t
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of 4096 rows of every linear (full-activation tensor scale, quantize, "
+                      f"dequantize, fp64-accumulated GEMM); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

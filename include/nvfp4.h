@@ -1,0 +1,151 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: NVFP4 block-scaled 4-bit quantization and FP4-packed GEMM
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Format [NVFP4-DiT page, Methodology section 1, Definition III.1; vllm-omni NVFP4 RFC,
+ * Motivation]: every run of 16 consecutive values along K (a "block") gets one OCP E4M3FN scale
+ * byte e, the whole tensor gets one fp32 scale S, and each value v becomes the 4-bit E2M1 code
+ * nearest to v / (e S) (grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} with sign, ties to the even code,
+ * saturating at +-6).  Readings fixed here where the pages are silent:
+ *   - dynamic S = RN32(max|x| / 2688), 2688 = 6 * 448; static S is given by the caller;
+ *   - e = E4M3 value nearest to max|block| / (6 S) (ties to even, saturating at 448, 0 for a
+ *     block that is zero or rounds to zero; such a block's codes carry only the sign);
+ *   - the code's sign bit copies the input's sign bit (so -0.0 gives code 8);
+ *   - decisions are made on exact real quotients (no intermediate rounding);
+ *   - element 2i of a row sits in the low nibble of byte i [NVFP4-DiT page, Methodology
+ *     section 3, two FP4 values per byte].
+ *
+ * Canonical layouts (row-major, K contiguous):
+ *   packed  uint8 [M][K/2]    scales  uint8 [M][K/16]    tensor scale  one fp32.
+ * GEMM: Y[M][N] = A[M][K] * B[N][K]^T ("TN"), B being the NVFP4 weight in a prepacked layout.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers owned by the caller (any allocator); the library
+ *     allocates, frees and retains nothing.  Tensor scales are device pointers too, so a
+ *     dynamic activation scale feeds the GEMM without a host synchronization.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous and ordered
+ *     on that stream; results are valid once the stream has reached them.
+ *   - Shape, stride, alignment, dtype, mode and workspace checks run on the host before any HIP
+ *     call; on failure the call returns the status and launches nothing.
+ *   - After launching, a HIP error is reported as NVFP4_ERR_HIP.
+ *   - Preconditions on device data are not checked: finite inputs; a static S that is finite
+ *     and > 0; scale bytes never 0x7F/0xFF.  Results are undefined when they fail.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,     /* M < 1, N < 1, K < 16, K % 16 != 0, or a size overflow */
+  NVFP4_ERR_STRIDE = 3,    /* a leading dimension is smaller than the row it must hold */
+  NVFP4_ERR_ALIGN = 4,     /* a pointer or row pitch breaks the stated alignment */
+  NVFP4_ERR_DTYPE = 5,     /* unknown dtype, or a dtype the call does not accept */
+  NVFP4_ERR_MODE = 6,      /* unknown mode */
+  NVFP4_ERR_WORKSPACE = 7, /* workspace required but NULL or smaller than the query says */
+  NVFP4_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed */
+  NVFP4_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
+
+/* W4A4: both operands NVFP4 [NVFP4-DiT page, Methodology section 3; vllm-omni RFC, Open
+   Question 1].  W4A16: bf16 activations times an NVFP4 weight (weight-only quantization,
+   vllm-omni RFC Open Question 1; kandinsky-5 NVFP4 pull request, Summary). */
+typedef enum { NVFP4_W4A4 = 0, NVFP4_W4A16 = 1 } nvfp4_mode_t;
+
+/* DYNAMIC: the call computes S from the input and writes it.  STATIC: the call reads a
+   caller-given S (the pages' static / calibrated scale: NVFP4-DiT page, Highlights, "Static FP4";
+   vllm-omni RFC, Open Question 2). */
+typedef enum { NVFP4_SCALE_DYNAMIC = 0, NVFP4_SCALE_STATIC = 1 } nvfp4_scale_mode_t;
+
+/* Short English text for a status; never NULL. */
+const char *nvfp4_status_string(nvfp4_status_t status);
+
+/* NVFP4_ABI_VERSION of the built library. */
+int nvfp4_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Quantize [NVFP4-DiT page, Definition III.1; vllm-omni RFC, Motivation].
+ *
+ *   x            device, [M][ld_x] elements of x_dtype (fp32 or bf16), 16-byte aligned,
+ *                ld_x * sizeof(elem) a multiple of 16.  Only the first K of each row are read.
+ *   M, K         M >= 1; K >= 16 and K % 16 == 0.
+ *   packed       device, [M][K/2] bytes, written.  8-byte aligned.
+ *   scales       device, [M][K/16] E4M3 bytes, written.
+ *   tensor_scale device, one fp32: written by DYNAMIC, read by STATIC (finite, > 0).
+ *   workspace    device scratch of nvfp4_quantize_workspace_bytes(M, K) bytes, 16-byte aligned
+ *                (DYNAMIC only; may be NULL for STATIC).  Its contents need no initialization
+ *                and are clobbered.
+ *
+ * The result is bit-identical to the definition above for every finite input.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K);
+nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                              uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                              nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Dequantize [NVFP4-DiT page, Definition III.1: Q = s * q]: y = RN32(q * e * S), one rounding
+ * of the exact product; bf16 output is the nearest bf16 (ties to even) of that fp32 value.
+ *
+ *   packed, scales, tensor_scale  canonical NVFP4 tensor as written by nvfp4_quantize
+ *                                 (packed 8-byte aligned).
+ *   y            device, [M][ld_y] of y_dtype, 16-byte aligned, ld_y * sizeof(elem) % 16 == 0,
+ *                ld_y >= K.  Columns K..ld_y-1 are not written.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                int64_t M, int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Weight prepack (offline, once per weight).  Rearranges a canonical NVFP4 weight [N][K]
+ * (packed [N][K/2], scales [N][K/16]) into the tile order the GEMM kernels read: N is padded
+ * to a multiple of 32 and K to a multiple of 128 with zero codes and zero scales.  The layout is
+ * opaque; its size is nvfp4_prepacked_bytes(N, K).  prepacked must be 16-byte aligned.  The
+ * weight's tensor scale is not part of it and is passed to nvfp4_gemm separately.
+ * nvfp4_unpack_weight is the exact inverse (for inspection and tests).
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_prepacked_bytes(int64_t N, int64_t K);
+nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                                    void *prepacked, void *stream);
+nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, uint8_t *packed,
+                                   uint8_t *scales, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * GEMM  Y = A * B^T  [NVFP4-DiT page, Methodology section 3: packed FP4 operands dequantized on
+ * the fly, FP32 accumulation].  Operands are dequantized exactly (each q * e is exact in 16-bit
+ * floating point) and multiplied on the matrix cores with fp32 accumulation; S_A * S_B is applied
+ * to the fp32 accumulator before the output conversion.  Only the summation order differs from
+ * the dequantize-then-matmul definition.
+ *
+ *   mode           NVFP4_W4A4: a = packed [M][lda/2] bytes, a_scales = [M][lda/16] E4M3 bytes,
+ *                  a_tensor_scale = device fp32 S_A (as written by nvfp4_quantize; lda == K for
+ *                  its output).  lda % 16 == 0, lda >= K.
+ *                  NVFP4_W4A16: a = bf16 [M][lda] (lda >= K, lda * 2 % 16 == 0, 16-byte aligned);
+ *                  a_scales and a_tensor_scale must be NULL.
+ *   b_prepacked    weight from nvfp4_prepack_weight(N, K); b_tensor_scale its device fp32 S_B.
+ *   c              device, [M][ldc] of c_dtype (fp32 or bf16), ldc >= N, base 16-byte aligned.
+ *   workspace      device scratch of nvfp4_gemm_workspace_bytes(mode, M, N, K) bytes (may be NULL
+ *                  when that is 0), 16-byte aligned; contents need no initialization.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
+nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,
+                          const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
+                          int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

@@ -1,0 +1,232 @@
+"""Python binding of libnvfp4 (NVFP4 quantize / dequantize / prepack / GEMM for MI355X, gfx950).
+
+Thin ctypes layer over the C ABI in ``include/nvfp4.h``: it allocates outputs and workspaces with
+PyTorch (device memory and streams only), passes raw device pointers and the current HIP stream,
+and turns a non-zero status into an exception.  Every step of the computation runs in the HIP
+kernels of ``libnvfp4.so``; there is no fallback.  The function names mirror the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from enum import IntEnum
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+
+class Status(IntEnum):
+    OK = 0
+    ERR_NULL = 1
+    ERR_SHAPE = 2
+    ERR_STRIDE = 3
+    ERR_ALIGN = 4
+    ERR_DTYPE = 5
+    ERR_MODE = 6
+    ERR_WORKSPACE = 7
+    ERR_HIP = 8
+    ERR_DEVICE = 9
+
+
+F32, BF16 = 0, 1
+W4A4, W4A16 = 0, 1
+SCALE_DYNAMIC, SCALE_STATIC = 0, 1
+
+EXPORTED = (
+    "nvfp4_status_string", "nvfp4_abi_version",
+    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
+    "nvfp4_dequantize",
+    "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
+    "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+)
+
+_lib = None
+_vp, _i64, _sz, _i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = Status(status)
+        super().__init__(f"{call}: {self.status.name} ({lib().nvfp4_status_string(status).decode()})")
+
+
+def lib():
+    """The loaded libnvfp4 (ctypes.CDLL).  Raises if the HIP library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libnvfp4.so not found at {LIB_PATH}; build it with "
+                           "`python nvfp4_quantized_gemm_amd/build.py` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [_i]
+    L.nvfp4_abi_version.restype = _i
+    L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_quantize_workspace_bytes.restype = _sz
+    L.nvfp4_quantize_workspace_bytes.argtypes = [_i64, _i64]
+    L.nvfp4_quantize.restype = _i
+    L.nvfp4_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+    L.nvfp4_dequantize.restype = _i
+    L.nvfp4_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i, _i64, _vp]
+    L.nvfp4_prepacked_bytes.restype = _sz
+    L.nvfp4_prepacked_bytes.argtypes = [_i64, _i64]
+    L.nvfp4_prepack_weight.restype = _i
+    L.nvfp4_prepack_weight.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+    L.nvfp4_unpack_weight.restype = _i
+    L.nvfp4_unpack_weight.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    L.nvfp4_gemm_workspace_bytes.restype = _sz
+    L.nvfp4_gemm_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
+    L.nvfp4_gemm.restype = _i
+    L.nvfp4_gemm.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _i64, _vp, _sz, _vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise NVFP4Error(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {dt}; libnvfp4 takes float32 or bfloat16")
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along K")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+# ---- quantize / dequantize ----------------------------------------------------------------------
+
+def nvfp4_quantize_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().nvfp4_quantize_workspace_bytes(M, K))
+
+
+def nvfp4_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *, static: bool | None = None,
+                   packed=None, scales=None, workspace=None, stream=None):
+    """Quantize x [M, K] (fp32 or bf16, device).
+
+    static=False (the default when tensor_scale is None): dynamic scale, computed on the device and
+    written to tensor_scale (allocated when None).  static=True (the default when tensor_scale is
+    given): tensor_scale holds the caller's S.  Returns (packed u8 [M, K/2], scales u8 [M, K/16],
+    S f32 [1])."""
+    M, K, ld = _rows(x, "x")
+    dev = x.device
+    if packed is None:
+        packed = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, max(K // 16, 0)), dtype=torch.uint8, device=dev)
+    if static is None:
+        static = tensor_scale is not None
+    dynamic = not static
+    if tensor_scale is None:
+        if static:
+            raise ValueError("static quantization needs tensor_scale")
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    S = tensor_scale
+    ws_bytes = 0
+    if dynamic:
+        ws_bytes = nvfp4_quantize_workspace_bytes(M, K)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), M, K, ld, _ptr(packed), _ptr(scales), _ptr(S),
+                              SCALE_DYNAMIC if dynamic else SCALE_STATIC, _ptr(workspace), ws_bytes,
+                              _stream(stream))
+    _check(st, "nvfp4_quantize")
+    return packed, scales, S
+
+
+def nvfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor,
+                     dtype: torch.dtype = torch.float32, *, out=None, stream=None) -> torch.Tensor:
+    M, K = packed.shape[0], packed.shape[1] * 2
+    if out is None:
+        out = torch.empty((M, K), dtype=dtype, device=packed.device)
+    _, _, ld = _rows(out, "out")
+    st = lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), _ptr(tensor_scale), M, K, _ptr(out),
+                                _dtype_code(out.dtype), ld, _stream(stream))
+    _check(st, "nvfp4_dequantize")
+    return out
+
+
+# ---- weight prepack -------------------------------------------------------------------------------
+
+def nvfp4_prepacked_bytes(N: int, K: int) -> int:
+    return int(lib().nvfp4_prepacked_bytes(N, K))
+
+
+def nvfp4_prepack_weight(packed: torch.Tensor, scales: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:
+    N, K = packed.shape[0], packed.shape[1] * 2
+    nbytes = nvfp4_prepacked_bytes(N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    st = lib().nvfp4_prepack_weight(_ptr(packed), _ptr(scales), N, K, _ptr(out), _stream(stream))
+    _check(st, "nvfp4_prepack_weight")
+    return out
+
+
+def nvfp4_unpack_weight(prepacked: torch.Tensor, N: int, K: int, *, stream=None):
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=prepacked.device)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=prepacked.device)
+    st = lib().nvfp4_unpack_weight(_ptr(prepacked), N, K, _ptr(packed), _ptr(scales), _stream(stream))
+    _check(st, "nvfp4_unpack_weight")
+    return packed, scales
+
+
+# ---- GEMM -------------------------------------------------------------------------------------------
+
+def nvfp4_gemm_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_workspace_bytes(mode, M, N, K))
+
+
+def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked: torch.Tensor,
+               b_tensor_scale: torch.Tensor, N: int, K: int, out_dtype: torch.dtype = torch.bfloat16, *,
+               out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Y = A B^T.  W4A4: a = packed u8 [M, K/2] with a_scales u8 [M, K/16] and a_tensor_scale
+    (from nvfp4_quantize).  W4A16: a = bf16 [M, K], a_scales = a_tensor_scale = None."""
+    M = a.shape[0]
+    if mode == W4A4:
+        lda = a.stride(0) * 2
+    else:
+        _, _, lda = _rows(a, "a")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    ldc = out.stride(0)
+    ws_need = nvfp4_gemm_workspace_bytes(mode, M, N, K)
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_gemm(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_prepacked),
+                          _ptr(b_tensor_scale), M, N, K, lda, _ptr(out), _dtype_code(out.dtype), ldc,
+                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_gemm")
+    return out
+
+
+__all__ = [
+    "Status", "NVFP4Error", "lib", "LIB_PATH", "EXPORTED", "F32", "BF16", "W4A4", "W4A16",
+    "SCALE_DYNAMIC", "SCALE_STATIC",
+    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
+    "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
+    "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+]

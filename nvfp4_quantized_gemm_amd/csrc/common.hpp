@@ -1,0 +1,72 @@
+// Device helpers shared by the libnvfp4 kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Largest finite E4M3FN magnitude and the dynamic-scale divisor 6 * 448.
+constexpr float kE4M3Max = 448.0f;
+constexpr float kDynDivisor = 2688.0f;
+
+// Fast-path validity window for the tensor scale: inside it every reciprocal used by the
+// quantizer's fast path is a normal fp32 value.
+constexpr float kFastSMin = 0x1p-100f;
+constexpr float kFastSMax = 0x1p+100f;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// OCP E4M3FN byte -> fp32 (hardware conversion; gfx950 decodes the OCP variant).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Hardware FP4 conversions; the byte-select operand must be a literal, hence the templates.
+// Encode: two fp32 -> two E2M1 codes (round-half-even, saturating at +-6, sign kept) into byte J.
+template <int J>
+__device__ __forceinline__ uint32_t fp4_encode2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, J);
+}
+// Decode byte J of `codes` (low nibble first) to exact values.
+template <int J>
+__device__ __forceinline__ f32x2 fp4_decode2_f32(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, J);
+}
+template <int J>
+__device__ __forceinline__ f16x2 fp4_decode2_f16(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, J);
+}
+
+// Magic-number unsigned division by a runtime constant d (1 <= d < 2^31).
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.shift = s;
+  f.mul = (uint32_t)((((1ull << 32) * ((1ull << s) - d)) / d) + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv &f) {
+  if (f.shift == 0) return n;  // d == 1
+  uint32_t t = __umulhi(n, f.mul);
+  return (t + ((n - t) >> 1)) >> (f.shift - 1);
+}
+
+}  // namespace nvfp4

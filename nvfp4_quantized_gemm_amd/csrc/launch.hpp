@@ -1,0 +1,42 @@
+// Internal interface between the C ABI (nvfp4_api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pass (= partials)
+constexpr int kQuantizeMaxGrid = 2048;  // grid cap of the quantize kernel (grid-stride beyond)
+constexpr int kDequantizeMaxGrid = 4096;
+
+hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+                           uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
+                             int64_t K, void *y, int out_dtype, int64_t ld_y, hipStream_t stream);
+
+hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, void *out,
+                          hipStream_t stream);
+hipError_t launch_unpack(const void *in, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales, hipStream_t stream);
+
+enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256 };
+
+struct GemmArgs {
+  int mode;  // 0 W4A4, 1 W4A16
+  const void *a;
+  const uint8_t *a_scales;
+  const float *a_ts;
+  const void *b;
+  const float *b_ts;
+  int64_t M, N, K, lda;
+  void *c;
+  int out_dtype;  // 0 f32, 1 bf16
+  int64_t ldc;
+  void *workspace;
+};
+
+GemmVariant select_gemm_variant(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,192 @@
+// libnvfp4 C ABI: argument validation (host only, before any HIP call), device check, dispatch.
+// Semantics and layouts are documented in include/nvfp4.h.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "launch.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // guards 64-bit size arithmetic
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+nvfp4_status_t check_mk(int64_t M, int64_t K) {
+  if (M < 1 || K < 16 || (K % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (M > kMaxElems / K) return NVFP4_ERR_SHAPE;
+  if (M * (K / 16) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;  // 32-bit block index
+  return NVFP4_OK;
+}
+
+int elem_size(nvfp4_dtype_t t) { return t == NVFP4_F32 ? 4 : 2; }
+bool valid_dtype(int t) { return t == NVFP4_F32 || t == NVFP4_BF16; }
+
+// The current device must be gfx950.  Queried once per device and cached.
+nvfp4_status_t check_device() {
+  static int cached_dev = -1;
+  static bool cached_ok = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
+  if (dev == cached_dev) return cached_ok ? NVFP4_OK : NVFP4_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_ERR_HIP;
+  cached_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  cached_dev = dev;
+  return cached_ok ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+nvfp4_status_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_status_string(nvfp4_status_t s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (M, N >= 1; K >= 16 and K % 16 == 0)";
+    case NVFP4_ERR_STRIDE: return "leading dimension too small";
+    case NVFP4_ERR_ALIGN: return "pointer or row pitch misaligned";
+    case NVFP4_ERR_DTYPE: return "unsupported dtype";
+    case NVFP4_ERR_MODE: return "unknown mode";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP runtime error";
+    case NVFP4_ERR_DEVICE: return "current device is not gfx950";
+  }
+  return "unknown status";
+}
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K) {
+  (void)M;
+  (void)K;
+  return (size_t)kAmaxPartials * sizeof(float);
+}
+
+nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                              uint8_t *packed, uint8_t *scales, float *tensor_scale, nvfp4_scale_mode_t mode,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !packed || !scales || !tensor_scale) return NVFP4_ERR_NULL;
+  if (!valid_dtype(x_dtype)) return NVFP4_ERR_DTYPE;
+  if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
+  nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (ld_x < K) return NVFP4_ERR_STRIDE;
+  const int es = elem_size(x_dtype);
+  if (!aligned(x, 16) || ((ld_x * es) % 16) != 0 || !aligned(packed, 8) || !aligned(tensor_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  if (mode == NVFP4_SCALE_DYNAMIC) {
+    if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, packed, scales, tensor_scale,
+                                    mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
+                                int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
+  if (!packed || !scales || !tensor_scale || !y) return NVFP4_ERR_NULL;
+  if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (ld_y < K) return NVFP4_ERR_STRIDE;
+  const int es = elem_size(y_dtype);
+  if (!aligned(y, 16) || ((ld_y * es) % 16) != 0 || !aligned(packed, 8) || !aligned(tensor_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(
+      launch_dequantize(packed, scales, tensor_scale, M, K, y, (int)y_dtype, ld_y, static_cast<hipStream_t>(stream)));
+}
+
+size_t nvfp4_prepacked_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 16 || (K % 16) != 0 || N > kMaxElems / K) return 0;
+  const int64_t Nu = (N + 31) / 32, Kc = (K + 127) / 128;
+  return (size_t)(Nu * Kc * (2048 + 256));
+}
+
+nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                                    void *prepacked, void *stream) {
+  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
+  nvfp4_status_t st = check_mk(N, K);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_prepack(packed, scales, N, K, prepacked, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                                   void *stream) {
+  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
+  nvfp4_status_t st = check_mk(N, K);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_unpack(prepacked, N, K, packed, scales, static_cast<hipStream_t>(stream)));
+}
+
+size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+  if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return 0;
+  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0) return 0;
+  return gemm_workspace_bytes((int)mode, M, N, K);
+}
+
+nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,
+                          const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
+                          int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return NVFP4_ERR_MODE;
+  if (!a || !b_prepacked || !b_tensor_scale || !c) return NVFP4_ERR_NULL;
+  if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
+  if (mode == NVFP4_W4A16 && (a_scales || a_tensor_scale)) return NVFP4_ERR_NULL;
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_DTYPE;
+  if (N < 1) return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
+  if (lda < K || ldc < N) return NVFP4_ERR_STRIDE;
+  if (mode == NVFP4_W4A4) {
+    if ((lda % 16) != 0) return NVFP4_ERR_STRIDE;
+    if (!aligned(a, 8)) return NVFP4_ERR_ALIGN;
+  } else {
+    if (!aligned(a, 16) || ((lda * 2) % 16) != 0) return NVFP4_ERR_ALIGN;
+  }
+  if (!aligned(b_prepacked, 16) || !aligned(c, 16) || !aligned(b_tensor_scale, 4)) return NVFP4_ERR_ALIGN;
+  const size_t need = nvfp4_gemm_workspace_bytes(mode, M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  GemmArgs g;
+  g.mode = (int)mode;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.a_ts = a_tensor_scale;
+  g.b = b_prepacked;
+  g.b_ts = b_tensor_scale;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.c = c;
+  g.out_dtype = (int)c_dtype;
+  g.ldc = ldc;
+  g.workspace = workspace;
+  return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments on the host before any HIP call (fake device pointers are
+never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_quantized_gemm_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+P = ctypes.c_void_p(0x10000)     # 16-byte aligned fake device pointer (never dereferenced)
+P8 = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+PODD = ctypes.c_void_p(0x10001)  # misaligned
+NULL = None
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return nv.lib()
+
+
+def test_exports_every_header_symbol(L):
+    funcs = header_functions()
+    assert len(funcs) >= 10
+    for f in funcs:
+        assert hasattr(L, f), f
+    assert sorted(funcs) == sorted(nv.EXPORTED)
+
+
+def test_version_and_status_strings(L):
+    assert L.nvfp4_abi_version() == 1
+    for s in nv.Status:
+        assert len(L.nvfp4_status_string(int(s))) > 0
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+def test_size_queries(L):
+    assert L.nvfp4_prepacked_bytes(1152, 1152) == 36 * 9 * 2304
+    assert L.nvfp4_prepacked_bytes(33, 16) == 2 * 1 * 2304
+    assert L.nvfp4_prepacked_bytes(0, 128) == 0
+    assert L.nvfp4_prepacked_bytes(32, 24) == 0
+    assert L.nvfp4_quantize_workspace_bytes(4096, 1152) >= 4
+    assert L.nvfp4_gemm_workspace_bytes(0, 4096, 1152, 1152) >= 0
+    assert L.nvfp4_gemm_workspace_bytes(7, 4096, 1152, 1152) == 0
+
+
+def q(L, x=P, dt=nv.BF16, M=4, K=32, ld=32, packed=P, scales=P, S=P, mode=nv.SCALE_DYNAMIC, ws=P, wsb=4096):
+    return L.nvfp4_quantize(x, dt, M, K, ld, packed, scales, S, mode, ws, wsb, None)
+
+
+def test_quantize_validation(L):
+    S = nv.Status
+    assert q(L, x=NULL) == S.ERR_NULL
+    assert q(L, packed=NULL) == S.ERR_NULL
+    assert q(L, S=NULL) == S.ERR_NULL
+    assert q(L, dt=7) == S.ERR_DTYPE
+    assert q(L, mode=5) == S.ERR_MODE
+    assert q(L, M=0) == S.ERR_SHAPE
+    assert q(L, K=24, ld=24) == S.ERR_SHAPE
+    assert q(L, K=0, ld=0) == S.ERR_SHAPE
+    assert q(L, ld=16) == S.ERR_STRIDE
+    assert q(L, x=PODD) == S.ERR_ALIGN
+    assert q(L, ld=36) == S.ERR_ALIGN            # 72-byte bf16 row pitch
+    assert q(L, packed=ctypes.c_void_p(0x10004)) == S.ERR_ALIGN
+    assert q(L, ws=NULL) == S.ERR_WORKSPACE
+    assert q(L, wsb=4) == S.ERR_WORKSPACE
+
+
+def test_dequantize_validation(L):
+    S = nv.Status
+    d = lambda **kw: L.nvfp4_dequantize(kw.get("p", P), kw.get("s", P), kw.get("ts", P), kw.get("M", 4),
+                                        kw.get("K", 32), kw.get("y", P), kw.get("dt", nv.F32), kw.get("ld", 32), None)
+    assert d(p=NULL) == S.ERR_NULL
+    assert d(y=NULL) == S.ERR_NULL
+    assert d(dt=3) == S.ERR_DTYPE
+    assert d(K=17) == S.ERR_SHAPE
+    assert d(ld=8) == S.ERR_STRIDE
+    assert d(y=PODD) == S.ERR_ALIGN
+    assert d(ld=33) == S.ERR_ALIGN
+
+
+def test_prepack_validation(L):
+    S = nv.Status
+    assert L.nvfp4_prepack_weight(NULL, P, 32, 128, P, None) == S.ERR_NULL
+    assert L.nvfp4_prepack_weight(P, P, 32, 120, P, None) == S.ERR_SHAPE
+    assert L.nvfp4_prepack_weight(P, P, 32, 128, P8, None) == S.ERR_ALIGN
+    assert L.nvfp4_unpack_weight(P, 0, 128, P, P, None) == S.ERR_SHAPE
+
+
+def g(L, mode=nv.W4A4, a=P, asc=P, ats=P, b=P, bts=P, M=64, N=64, K=128, lda=128, c=P, dt=nv.BF16, ldc=64,
+      ws=NULL, wsb=0):
+    return L.nvfp4_gemm(mode, a, asc, ats, b, bts, M, N, K, lda, c, dt, ldc, ws, wsb, None)
+
+
+def test_gemm_validation(L):
+    S = nv.Status
+    assert g(L, mode=9) == S.ERR_MODE
+    assert g(L, a=NULL) == S.ERR_NULL
+    assert g(L, asc=NULL) == S.ERR_NULL
+    assert g(L, mode=nv.W4A16) == S.ERR_NULL    # W4A16 must not pass A scales
+    assert g(L, dt=4) == S.ERR_DTYPE
+    assert g(L, N=0) == S.ERR_SHAPE
+    assert g(L, K=100, lda=112) == S.ERR_SHAPE
+    assert g(L, lda=64) == S.ERR_STRIDE
+    assert g(L, ldc=32) == S.ERR_STRIDE
+    assert g(L, lda=136) == S.ERR_STRIDE       # W4A4 row pitch must hold whole scale blocks
+    assert g(L, b=P8) == S.ERR_ALIGN
+    assert g(L, c=PODD) == S.ERR_ALIGN
+    assert g(L, mode=nv.W4A16, asc=NULL, ats=NULL, a=P8) == S.ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(nv, "_lib", None)
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libnvfp4.so not found"):
+        nv.lib()

@@ -1,0 +1,335 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on identical seeded inputs.
+
+Bars: quantize, dequantize and prepack bit-exact (codes, scale bytes, tensor scale, output bit
+patterns including the sign of zero); GEMM |Y_gpu - Y| <= 1e-5 * sum_k |a_ik b_jk| per element for
+fp32 output (only the summation order differs), plus the output rounding 2^-8 |Y| for bf16 output.
+Every output buffer sits between canary guard bands that must stay untouched.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantized_gemm_amd as nv
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GUARD = 256
+CANARY = 0xA5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---- helpers ------------------------------------------------------------------------------------
+
+def np_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def np_x(t: torch.Tensor) -> np.ndarray:
+    """Oracle view of an input tensor: float32 stays float32, bf16 becomes its bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return np_bf16(t)
+    return t.detach().cpu().contiguous().numpy()
+
+
+class Guarded:
+    """A device byte buffer with canary bands around the payload."""
+
+    def __init__(self, nbytes: int):
+        self.n = nbytes
+        self.buf = torch.full((nbytes + 2 * GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+
+    def payload(self, shape, dtype=torch.uint8):
+        return self.buf[GUARD:GUARD + self.n].view(dtype).view(shape)
+
+    def check(self):
+        b = self.buf.cpu().numpy()
+        assert (b[:GUARD] == CANARY).all() and (b[GUARD + self.n:] == CANARY).all(), "guard band overwritten"
+
+
+def gpu_quantize(x_cpu: torch.Tensor, static_S=None, ld=None):
+    M, K = x_cpu.shape
+    if ld is not None and ld != K:
+        big = torch.zeros((M, ld), dtype=x_cpu.dtype)
+        big[:, :K] = x_cpu
+        big[:, K:] = 1e30 if x_cpu.dtype == torch.float32 else 1e30  # must be ignored
+        xd = big.to(DEV)[:, :K]
+    else:
+        xd = x_cpu.to(DEV)
+    gp, gs = Guarded(M * K // 2), Guarded(M * K // 16)
+    Sd = None if static_S is None else torch.tensor([static_S], dtype=torch.float32, device=DEV)
+    p, s, S = nv.nvfp4_quantize(xd, Sd, packed=gp.payload((M, K // 2)), scales=gs.payload((M, K // 16)))
+    torch.cuda.synchronize()
+    gp.check()
+    gs.check()
+    return p.cpu().numpy(), s.cpu().numpy(), np.float32(S.item()), (p, s, S)
+
+
+def assert_quantize_exact(x_cpu, static_S=None, ld=None, label=""):
+    say(f"[quantize] {label} shape={tuple(x_cpu.shape)} dtype={x_cpu.dtype} static={static_S} ld={ld}")
+    gp_, gs_, gS, dev = gpu_quantize(x_cpu, static_S, ld)
+    op, os_, oS = oracle.quantize(np_x(x_cpu), S=static_S)
+    assert np.float32(gS).view(np.uint32) == np.float32(oS).view(np.uint32), (gS, oS)
+    bad_s = np.nonzero(gs_ != os_)
+    assert bad_s[0].size == 0, f"{bad_s[0].size} scale bytes differ, first at {bad_s[0][0], bad_s[1][0]}"
+    bad_p = np.nonzero(gp_ != op)
+    assert bad_p[0].size == 0, f"{bad_p[0].size} code bytes differ, first at {bad_p[0][0], bad_p[1][0]}"
+    return dev, (op, os_, oS)
+
+
+# ---- quantize -------------------------------------------------------------------------------------
+
+def test_quantize_tiny_fp32_dynamic():
+    x, w = workloads.tiny()
+    assert_quantize_exact(x, label="tiny X")
+    assert_quantize_exact(w, label="tiny W")
+
+
+@pytest.mark.parametrize("M,K", [(4096, 1152), (4096, 3072)])
+def test_quantize_sweep_dynamic_and_static(M, K):
+    x = workloads.sweep(M, K)
+    assert_quantize_exact(x, label="sweep dynamic")
+    xs = workloads.sweep(M, K, static=True)
+    assert_quantize_exact(xs, static_S=workloads.SWEEP_STATIC_S, label="sweep static")
+
+
+@pytest.mark.parametrize("M,K,ld,dt", [
+    (1, 16, 16, torch.bfloat16), (1, 16, 16, torch.float32), (17, 48, 56, torch.bfloat16),
+    (255, 1168, 1168, torch.bfloat16), (3, 4096, 4104, torch.bfloat16), (33, 80, 84, torch.float32),
+    (1000, 272, 272, torch.float32),
+])
+def test_quantize_ragged_shapes_and_strides(M, K, ld, dt):
+    g = torch.Generator().manual_seed(M * 7 + K)
+    x = torch.randn(M, K, generator=g) * torch.exp(3 * torch.randn(M, 1, generator=g))
+    x[0, :16] = 0.0
+    if M > 1:
+        x[1, :16] = -0.0
+    x = x.to(dt)
+    assert_quantize_exact(x, ld=ld, label="ragged dynamic")
+    assert_quantize_exact(x, static_S=0.0123, ld=ld, label="ragged static")
+
+
+def test_quantize_all_zero_tensor():
+    x = torch.zeros(8, 64, dtype=torch.bfloat16)
+    x[3, 5] = -0.0
+    dev, (op, os_, oS) = assert_quantize_exact(x, label="all zero")
+    assert oS == 0.0 and (os_ == 0).all()
+
+
+def test_quantize_extreme_static_scales():
+    """Static S far outside the fast-path window exercises the exact threshold path everywhere."""
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(64, 128, generator=g) * 1e-30).to(torch.float32)
+    assert_quantize_exact(x, static_S=2.0 ** -120, label="tiny S")
+    x = (torch.randn(64, 128, generator=g) * 1e30).to(torch.float32)
+    assert_quantize_exact(x, static_S=2.0 ** 110, label="huge S")
+
+
+def test_quantize_sweep_full_size_largest():
+    """Largest sweep tensor (32768 x 12288 bf16, 403M values), dynamic, full comparison."""
+    x = workloads.sweep(32768, 12288)
+    assert_quantize_exact(x, label="sweep 32768x12288")
+
+
+def test_quantize_deterministic():
+    x = workloads.sweep(4096, 1152)
+    a = gpu_quantize(x)
+    b = gpu_quantize(x)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all() and a[2] == b[2]
+
+
+# ---- dequantize -------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(4096, 1152), (17, 48)])
+def test_dequantize_exact_bits(M, K):
+    x = workloads.sweep(M, K) if M >= 4096 else torch.randn(M, K, generator=torch.Generator().manual_seed(3)).to(
+        torch.bfloat16)
+    say(f"[dequantize] {M}x{K}")
+    (p, s, S), (op, os_, oS) = assert_quantize_exact(x, label="for dequant")
+    y32_o, y16_o = oracle.dequantize(op, os_, oS)
+    for dt, ref in ((torch.float32, y32_o.view(np.uint32)), (torch.bfloat16, y16_o)):
+        esz = 4 if dt == torch.float32 else 2
+        ld = K + (16 // esz)  # padded rows: the pad must stay untouched
+        gy = Guarded(M * ld * esz)
+        out = gy.payload((M, ld), dt)
+        out_view = out[:, :K]
+        nv.nvfp4_dequantize(p, s, S, dt, out=out_view)
+        torch.cuda.synchronize()
+        gy.check()
+        raw = gy.buf[GUARD:GUARD + M * ld * esz].cpu().numpy()
+        if dt == torch.float32:
+            bits = raw.view(np.uint32).reshape(M, ld)
+        else:
+            bits = raw.view(np.uint16).reshape(M, ld)
+        np.testing.assert_array_equal(bits[:, :K], ref)
+        pad = raw.reshape(M, ld * esz)[:, K * esz:]
+        assert (pad == CANARY).all(), "row padding written"
+
+
+def test_requantize_roundtrip_on_gpu():
+    """Quantize -> dequantize (fp32) -> quantize with the same static S reproduces bytes 0 and >= 3."""
+    x = workloads.sweep(4096, 1152)
+    (p, s, S), (op, os_, oS) = assert_quantize_exact(x, label="roundtrip")
+    y = nv.nvfp4_dequantize(p, s, S, torch.float32)
+    p2, s2, _ = nv.nvfp4_quantize(y, S)
+    s_np, s2_np = s.cpu().numpy().ravel(), s2.cpu().numpy().ravel()
+    keep = (s_np == 0) | (s_np >= 3)
+    np.testing.assert_array_equal(s2_np[keep], s_np[keep])
+    np.testing.assert_array_equal(p2.cpu().numpy().reshape(-1, 8)[keep], p.cpu().numpy().reshape(-1, 8)[keep])
+
+
+# ---- prepack --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(32, 128), (33, 144), (1152, 1152), (100, 16), (3072, 12288)])
+def test_prepack_roundtrip(N, K):
+    g = torch.Generator().manual_seed(N + K)
+    packed = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8)
+    scales = torch.randint(0, 0x7F, (N, K // 16), generator=g, dtype=torch.uint8)
+    pp = nv.nvfp4_prepack_weight(packed.to(DEV), scales.to(DEV))
+    assert pp.numel() == nv.nvfp4_prepacked_bytes(N, K)
+    up, us = nv.nvfp4_unpack_weight(pp, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(up.cpu(), packed) and torch.equal(us.cpu(), scales)
+
+
+# ---- GEMM -------------------------------------------------------------------------------------------
+
+def check_gemm(Yg: np.ndarray, Y: np.ndarray, R: np.ndarray, bf16_out: bool, label: str):
+    err = np.abs(Yg.astype(np.float64) - Y)
+    tol = 1e-5 * R
+    if bf16_out:
+        tol = 2.0 ** -8 * np.abs(Y) + 1.01e-5 * R
+    tol = tol + 1e-30  # all-zero rows
+    bad = err > tol
+    if bad.any():
+        i = np.argmax(err / tol)
+        raise AssertionError(f"{label}: {int(bad.sum())} of {bad.size} outside tolerance; worst "
+                             f"flat index {i}: gpu {Yg.flat[i]} ref {Y.flat[i]} R {R.flat[i]}")
+    say(f"  {label}: max err/R = {float(np.max(err / (R + 1e-30))):.3e}")
+
+
+def prepare_weight(w_cpu: torch.Tensor):
+    p, s, S, _ = gpu_quantize(w_cpu)
+    pd, sd, Sd = [torch.from_numpy(a).to(DEV) for a in (p, s)] + [torch.tensor([S], device=DEV)]
+    bp = nv.nvfp4_prepack_weight(pd, sd)
+    return bp, Sd, (p, s, S)
+
+
+def run_w4a4(x_cpu, w_cpu, out_dtype, sample=None):
+    M, K = x_cpu.shape
+    N = w_cpu.shape[0]
+    say(f"[gemm W4A4] M={M} N={N} K={K} out={out_dtype} sample={sample}")
+    bp, Sb, (wp, ws, wS) = prepare_weight(w_cpu)
+    xd = x_cpu.to(DEV)
+    pa, sa, Sa = nv.nvfp4_quantize(xd)
+    esz = 4 if out_dtype == torch.float32 else 2
+    gy = Guarded(M * N * esz)
+    out = gy.payload((M, N), out_dtype)
+    nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bp, Sb, N, K, out_dtype, out=out)
+    torch.cuda.synchronize()
+    gy.check()
+    Yg = out.float().cpu().numpy()
+    # oracle: its own quantization of both operands, dequantize, fp64 matmul
+    xo = np_x(x_cpu)
+    SA = oracle.tensor_scale(xo)
+    assert SA == np.float32(Sa.item())
+    if sample is None:
+        ap, as_, _ = oracle.quantize(xo, S=SA)
+        A, _ = oracle.dequantize(ap, as_, SA)
+        bo_p, bo_s, SB = oracle.quantize(np_x(w_cpu))
+        B, _ = oracle.dequantize(bo_p, bo_s, SB)
+        Y, R = oracle.gemm(A, B)
+        check_gemm(Yg, Y, R, out_dtype == torch.bfloat16, f"W4A4 {M}x{N}x{K}")
+    else:
+        rng = np.random.default_rng(M + N + K)
+        rows = np.unique(rng.integers(0, M, sample[0]))
+        cols = np.unique(rng.integers(0, N, sample[1]))
+        ap, as_, _ = oracle.quantize(np.ascontiguousarray(xo[rows]), S=SA)
+        A, _ = oracle.dequantize(ap, as_, SA)
+        SB = oracle.tensor_scale(np_x(w_cpu))
+        bo_p, bo_s, _ = oracle.quantize(np.ascontiguousarray(np_x(w_cpu)[cols]), S=SB)
+        B, _ = oracle.dequantize(bo_p, bo_s, SB)
+        Y, R = oracle.gemm(A, B)
+        check_gemm(Yg[np.ix_(rows, cols)], Y, R, out_dtype == torch.bfloat16, f"W4A4 {M}x{N}x{K} sampled")
+    return out
+
+
+def test_gemm_w4a4_tiny_full():
+    x, w = workloads.tiny()
+    run_w4a4(x, w, torch.float32)
+    run_w4a4(x, w, torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (17, 33, 144), (255, 100, 1152), (300, 520, 256),
+                                   (64, 64, 16), (129, 257, 384), (1000, 1000, 1280)])
+def test_gemm_w4a4_ragged(M, N, K):
+    g = torch.Generator().manual_seed(M + 3 * N + 7 * K)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    run_w4a4(x, w, torch.float32)
+
+
+def test_gemm_w4a4_pixart_full_size_sampled():
+    for name, x, w in workloads.pixart():
+        run_w4a4(x, w, torch.bfloat16, sample=(96, 96))
+
+
+def test_gemm_w4a4_video_full_size_sampled():
+    for name, x, w in workloads.video():
+        run_w4a4(x, w, torch.bfloat16, sample=(48, 48))
+
+
+def test_gemm_deterministic():
+    x, w = workloads.tiny()
+    a = run_w4a4(x, w, torch.float32).cpu()
+    b = run_w4a4(x, w, torch.float32).cpu()
+    assert torch.equal(a, b)
+
+
+def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
+    M, K = a_cpu.shape
+    N = w_cpu.shape[0]
+    say(f"[gemm W4A16] M={M} N={N} K={K} sample={sample}")
+    bp, Sb, _ = prepare_weight(w_cpu)
+    ad = a_cpu.to(DEV)
+    esz = 4 if out_dtype == torch.float32 else 2
+    gy = Guarded(M * N * esz)
+    out = gy.payload((M, N), out_dtype)
+    nv.nvfp4_gemm(nv.W4A16, ad, None, None, bp, Sb, N, K, out_dtype, out=out)
+    torch.cuda.synchronize()
+    gy.check()
+    Yg = out.float().cpu().numpy()
+    A = oracle.bf16_to_f32(np_bf16(a_cpu))
+    wo = np_x(w_cpu)
+    SB = oracle.tensor_scale(wo)
+    if sample is None:
+        cols = np.arange(N)
+    else:
+        cols = np.unique(np.random.default_rng(N + K).integers(0, N, sample))
+    bo_p, bo_s, _ = oracle.quantize(np.ascontiguousarray(wo[cols]), S=SB)
+    B, _ = oracle.dequantize(bo_p, bo_s, SB)
+    Y, R = oracle.gemm(A, B)
+    check_gemm(Yg[:, cols], Y, R, out_dtype == torch.bfloat16, f"W4A16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 96, 256), (37, 200, 1152), (300, 130, 384), (5, 48, 80)])
+def test_gemm_w4a16_ragged(M, N, K):
+    g = torch.Generator().manual_seed(M * 5 + N + K)
+    a = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = workloads.laplace_tailed_weight(N, K, g)
+    run_w4a16(a, w, torch.float32)
+
+
+def test_gemm_w4a16_full_size():
+    for name, (w, acts) in workloads.w4a16().items():
+        for m, a in acts.items():
+            run_w4a16(a, w, torch.bfloat16, sample=None if m <= 16 else 64)
