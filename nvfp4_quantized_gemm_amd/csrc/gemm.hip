@@ -19,6 +19,8 @@
 // sides.  Dequantization in registers: v_cvt_scalef32_pk_{f16,f32}_fp4 with scale 1 gives exact q;
 // one multiply by the block's E4M3 scale gives q * e.  The epilogue multiplies the fp32
 // accumulator by S_A * S_B and converts.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,7 +71,30 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
   else static_cast<__bf16 *>(c)[row * ldc + col] = (__bf16)v;
 }
 
-// MODE 0 = W4A4 (fp16 MFMA), 1 = W4A16 (bf16 MFMA).  WM x WN waves.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS copies (gfx950 LDS-DMA): every lane supplies its own global address; the
+// wave's data lands contiguously at `lds` (lane i at lds + i * size).  `lds` must be wave-uniform.
+__device__ __forceinline__ void g2l16(const void *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l4(const void *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// MODE 0 = W4A4 (fp16 MFMA), 1 = W4A16 (bf16 MFMA).  WM x WN waves of (BM/WM) x (BN/WN).
+//
+// LDS stage layout (one per buffer, two buffers):
+//   A codes   [BM/32][2 parts][64 lanes][16 B]   (MODE 0)  or  A bf16 [BM/32][8 steps][64 lanes][16 B]
+//   A scales  [BM/32][64 lanes][4 B]             (MODE 0)
+//   B codes   [BN/32][2 parts][64 lanes][16 B]   B scales [BN/32][64 lanes][4 B]
+// Each 1-KB (or 256-B) block is filled by one wave-wide LDS-DMA load whose lane addresses implement
+// the row-major -> lane-order permutation for A; B is prepacked in exactly this order.  Rows past
+// M and columns past N are clamped to the last valid one (their results are never stored).
+// Per chunk a wave first reads all of its fragments for the chunk into registers, then issues the
+// next chunk's loads into the other buffer, then runs its 8 MFMA steps from registers.
 template <int MODE, int BM, int BN, int WM, int WN, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
@@ -78,11 +103,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using Cfg = TileCfg<MODE, BM, BN>;
   constexpr int TM = BM / WM / 32;  // MFMA tiles per wave along M
   constexpr int TN = BN / WN / 32;
+  constexpr int NA = (MODE == 0) ? (BM / 32) * 2 : (BM / 32) * 8;  // 1-KB A blocks per stage
+  constexpr int NAS = (MODE == 0) ? BM / 32 : 0;                    // 256-B A scale blocks
+  constexpr int NB = (BN / 32) * 2, NBS = BN / 32;
+  static_assert(NA % 4 == 0 && NB % 4 == 0 && NBS % 4 == 0 && NAS % 4 == 0, "block counts");
+  constexpr int kAStep = (MODE == 0) ? 64 : 256;  // A bytes per row per chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   // XCD-aware tile order: consecutive dispatches land on different XCDs; give each XCD a
@@ -97,99 +126,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
   const int Kc = K / kChunk;
-  const int64_t Nu = ((int64_t)N + 31) / 32;
+  const int Nu = (N + 31) / 32;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
+  const int lh = lane >> 5, lr = lane & 31;
 
-  // ---- global -> register staging -------------------------------------------------------------
-  u32x4 ra[Cfg::kAIters];
-  uint32_t ras[2];
-  u32x4 rb[Cfg::kBIters];
-  u32x4 rbs;
-
-  auto load_chunk = [&](int kc) {
+  // ---- per-lane source addresses of this wave's LDS-DMA loads (chunk 0) -------------------------
+  const uint8_t *pa[NA / 4];
+  const uint8_t *pas[NAS / 4 > 0 ? NAS / 4 : 1];
+  const uint8_t *pb[NB / 4];
+  const uint8_t *pbs[NBS / 4];
+#pragma unroll
+  for (int i = 0; i < NA / 4; ++i) {
+    const int q = wave + 4 * i;
     if (MODE == 0) {
-      const uint8_t *A = static_cast<const uint8_t *>(a);
-#pragma unroll
-      for (int it = 0; it < Cfg::kAIters; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 2, cq = idx & 3;
-        const int64_t row = m0 + r;
-        if (row < M) ra[it] = *reinterpret_cast<const u32x4 *>(A + row * (lda / 2) + kc * 64 + 16 * cq);
-        else ra[it] = (u32x4){0u, 0u, 0u, 0u};
-      }
-      if (tid < BM) {
-        const int64_t row = m0 + tid;
-        if (row < M) {
-          const u32x2 s = *reinterpret_cast<const u32x2 *>(a_scales + row * (lda / 16) + kc * 8);
-          ras[0] = s.x;
-          ras[1] = s.y;
-        } else {
-          ras[0] = ras[1] = 0u;
-        }
-      }
+      const int sub = q >> 1, part = q & 1;
+      const int row = min(m0 + sub * 32 + lr, M - 1);
+      pa[i] = static_cast<const uint8_t *>(a) + (int64_t)row * (lda / 2) + 32 * lh + 16 * part;
     } else {
-      const uint16_t *A = static_cast<const uint16_t *>(a);
+      const int sub = q >> 3, st = q & 7;
+      const int row = min(m0 + sub * 32 + lr, M - 1);
+      pa[i] = reinterpret_cast<const uint8_t *>(static_cast<const uint16_t *>(a) + (int64_t)row * lda + 64 * lh + 8 * st);
+    }
+  }
 #pragma unroll
-      for (int it = 0; it < Cfg::kAIters; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 4, cq = idx & 15;
-        const int64_t row = m0 + r;
-        if (row < M) ra[it] = *reinterpret_cast<const u32x4 *>(A + row * lda + (int64_t)kc * kChunk + 8 * cq);
-        else ra[it] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
+  for (int i = 0; i < NAS / 4; ++i) {
+    const int q = wave + 4 * i;
+    const int row = min(m0 + q * 32 + lr, M - 1);
+    pas[i] = a_scales + (int64_t)row * (lda / 16) + 4 * lh;
+  }
 #pragma unroll
-    for (int it = 0; it < Cfg::kBIters; ++it) {
-      const int idx = it * 256 + tid;
-      const int u = idx >> 7, off = idx & 127;
-      const int64_t nu = n0 / 32 + u;
-      if (nu < Nu)
-        rb[it] = *reinterpret_cast<const u32x4 *>(bp + ((uint64_t)nu * Kc + kc) * 2048ull + 16ull * off);
-      else
-        rb[it] = (u32x4){0u, 0u, 0u, 0u};
-    }
-    if (tid < Cfg::kBSChunks) {
-      const int u = tid >> 4, off = tid & 15;
-      const int64_t nu = n0 / 32 + u;
-      if (nu < Nu)
-        rbs = *reinterpret_cast<const u32x4 *>(bp + scale_region + ((uint64_t)nu * Kc + kc) * 256ull + 16ull * off);
-      else
-        rbs = (u32x4){0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < NB / 4; ++i) {
+    const int q = wave + 4 * i;
+    const int nu = min(n0 / 32 + (q >> 1), Nu - 1);
+    pb[i] = bp + (uint64_t)nu * (uint64_t)Kc * 2048ull + (q & 1) * 1024 + lane * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < NBS / 4; ++i) {
+    const int q = wave + 4 * i;
+    const int nu = min(n0 / 32 + q, Nu - 1);
+    pbs[i] = bp + scale_region + (uint64_t)nu * (uint64_t)Kc * 256ull + lane * 4;
+  }
+
+  auto issue = [&](int kc, int buf) {
+    uint8_t *st = smem + buf * Cfg::kStage;
+#pragma unroll
+    for (int i = 0; i < NA / 4; ++i) g2l16(pa[i] + (int64_t)kc * kAStep, st + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < NAS / 4; ++i) g2l4(pas[i] + kc * 8, st + Cfg::kALds + (wave + 4 * i) * 256);
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i)
+      g2l16(pb[i] + (int64_t)kc * 2048, st + Cfg::kALds + Cfg::kASLds + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < NBS / 4; ++i)
+      g2l4(pbs[i] + (int64_t)kc * 256, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (wave + 4 * i) * 256);
   };
 
-  auto store_chunk = [&](int buf) {
+  // One of this wave's NSLOT DMA loads of chunk kc (t is a compile-time slot index).
+  constexpr int NSLOT = NA / 4 + NAS / 4 + NB / 4 + NBS / 4;
+  auto issue_slot = [&](int kc, int buf, int t) {
     uint8_t *st = smem + buf * Cfg::kStage;
-    uint8_t *sA = st, *sAS = st + Cfg::kALds, *sB = sAS + Cfg::kASLds, *sBS = sB + Cfg::kBLds;
-    if (MODE == 0) {
-#pragma unroll
-      for (int it = 0; it < Cfg::kAIters; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 2, cq = idx & 3;
-        const int sub = r >> 5, ln = (r & 31) + 32 * (cq >> 1), part = cq & 1;
-        *reinterpret_cast<u32x4 *>(sA + ((sub * 2 + part) * 64 + ln) * 16) = ra[it];
-      }
-      if (tid < BM) {
-        const int sub = tid >> 5, ln = tid & 31;
-        *reinterpret_cast<uint32_t *>(sAS + (sub * 64 + ln) * 4) = ras[0];
-        *reinterpret_cast<uint32_t *>(sAS + (sub * 64 + ln + 32) * 4) = ras[1];
-      }
+    if (t < NA / 4) {
+      g2l16(pa[t] + (int64_t)kc * kAStep, st + (wave + 4 * t) * 1024);
+    } else if (t < NA / 4 + NAS / 4) {
+      const int i = t - NA / 4;
+      g2l4(pas[i] + kc * 8, st + Cfg::kALds + (wave + 4 * i) * 256);
+    } else if (t < NA / 4 + NAS / 4 + NB / 4) {
+      const int i = t - NA / 4 - NAS / 4;
+      g2l16(pb[i] + (int64_t)kc * 2048, st + Cfg::kALds + Cfg::kASLds + (wave + 4 * i) * 1024);
     } else {
-#pragma unroll
-      for (int it = 0; it < Cfg::kAIters; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx >> 4, cq = idx & 15;  // cq: 16-B piece (8 k) of the row's 128 k
-        const int sub = r >> 5, h = cq >> 3, s = cq & 7;
-        const int ln = (r & 31) + 32 * h;
-        *reinterpret_cast<u32x4 *>(sA + ((sub * 8 + s) * 64 + ln) * 16) = ra[it];
-      }
+      const int i = t - NA / 4 - NAS / 4 - NB / 4;
+      g2l4(pbs[i] + (int64_t)kc * 256, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (wave + 4 * i) * 256);
     }
-#pragma unroll
-    for (int it = 0; it < Cfg::kBIters; ++it) {
-      const int idx = it * 256 + tid;
-      *reinterpret_cast<u32x4 *>(sB + idx * 16) = rb[it];
-    }
-    if (tid < Cfg::kBSChunks) *reinterpret_cast<u32x4 *>(sBS + tid * 16) = rbs;
   };
 
   f32x16 acc[TM][TN];
@@ -200,108 +207,215 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
+  if (MODE == 0) {
+    // ---- W4A4: one continuous stream of 16-k steps.  Step s+1 is dequantized while step s's 16
+    // MFMAs run (also across chunk boundaries).  Codes are held per half-chunk ("part", 4 steps):
+    // part 1 of chunk kc is read at the start of chunk kc, part 0 of chunk kc+1 (and its scales) at
+    // step 3, so every LDS read has >= 3 steps of MFMA work to land.  A 3-stage LDS ring with the
+    // DMA two chunks ahead leaves one barrier per chunk.
+    u32x4 P0a[TM], P0b[TN], P1a[TM], P1b[TN];
+    uint32_t Sa[TM], Sb[TN];
+    f16x2 Ea[TM][2], Eb[TN][2], Na[TM][2], Nb[TN][2];
+    f16x8 Fa[2][TM], Fb[2][TN];
 
-  for (int kc = 0; kc < Kc; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < Kc) load_chunk(kc + 1);
-
-    const uint8_t *st = smem + buf * Cfg::kStage;
-    const uint8_t *sA = st, *sAS = st + Cfg::kALds, *sB = sAS + Cfg::kASLds, *sBS = sB + Cfg::kBLds;
-
-    // per-chunk scale registers
-    uint32_t bsw[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int unit = (wn * (BN / WN)) / 32 + j;
-      bsw[j] = *reinterpret_cast<const uint32_t *>(sBS + (unit * 64 + lane) * 4);
-    }
-    uint32_t asw[TM];
-    if (MODE == 0) {
+    auto stage = [&](int buf) { return smem + buf * Cfg::kStage; };
+    auto read_part = [&](u32x4 *ra, u32x4 *rb, int buf, int part) {
+      const uint8_t *st = stage(buf);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int sub = (wm * (BM / WM)) / 32 + i;
-        asw[i] = *reinterpret_cast<const uint32_t *>(sAS + (sub * 64 + lane) * 4);
+        const int sub = wm * (BM / WM / 32) + i;
+        ra[i] = *reinterpret_cast<const u32x4 *>(st + ((sub * 2 + part) * 64 + lane) * 16);
       }
-    }
-
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {  // two parts of 4 MFMA steps each
-      u32x4 bc[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int unit = (wn * (BN / WN)) / 32 + j;
-        bc[j] = *reinterpret_cast<const u32x4 *>(sB + ((unit * 2 + p) * 64 + lane) * 16);
+        const int unit = wn * (BN / WN / 32) + j;
+        rb[j] = *reinterpret_cast<const u32x4 *>(st + Cfg::kALds + Cfg::kASLds + ((unit * 2 + part) * 64 + lane) * 16);
       }
-      u32x4 ac[TM];
-      if (MODE == 0) {
+    };
+    auto read_scales = [&](int buf) {
+      const uint8_t *st = stage(buf);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int sub = wm * (BM / WM / 32) + i;
+        Sa[i] = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + (sub * 64 + lane) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int unit = wn * (BN / WN / 32) + j;
+        Sb[j] = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (unit * 64 + lane) * 4);
+      }
+    };
+    auto cvt_scales = [&](f16x2 (*ea)[2], f16x2 (*eb)[2]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        ea[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sa[i], 1.0f, false);
+        ea[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sa[i], 1.0f, true);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        eb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[j], 1.0f, false);
+        eb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[j], 1.0f, true);
+      }
+    };
+    // dequantize step s (0..7) of a chunk from part registers (ra, rb) with scales (ea, eb)
+    auto deq = [&](const u32x4 *ra, const u32x4 *rb, f16x2 (*ea)[2], f16x2 (*eb)[2], int s, int slot) {
+      const int q = s & 3, blk = s >> 1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) Fa[slot][i] = dequant_f16x8(ra[i][q], ea[i][blk >> 1][blk & 1]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Fb[slot][j] = dequant_f16x8(rb[j][q], eb[j][blk >> 1][blk & 1]);
+    };
+    auto mfma_step = [&](int slot) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Fa[slot][i], Fb[slot][j], acc[i][j], 0, 0, 0);
+    };
+    auto interleave = [&]() {
+#pragma unroll
+      for (int t = 0; t < TM * TN; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (TM + TN)) / (TM * TN) + 1, 0);  // VALU
+      }
+    };
+
+    issue(0, 0);
+    if (Kc > 1) issue(1, 1);
+    wait_vmem();
+    __syncthreads();
+    read_part(P0a, P0b, 0, 0);
+    read_scales(0);
+    cvt_scales(Ea, Eb);
+    deq(P0a, P0b, Ea, Eb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int kc = 0; kc < Kc; ++kc) {
+      const int cur = kc % 3;
+      if (kc > 0) {
+        wait_vmem();  // this wave's DMA of chunk kc+1 (issued one chunk ago) has landed
+        __syncthreads();
+      }
+      // Branch-free steps (a branch would split the scheduling region): near the end of K the
+      // DMA re-fetches the last chunk into the free stage and the look-ahead reads/dequantizes a
+      // stale stage; neither result is used.
+      const int kdma = min(kc + 2, Kc - 1);
+      const int bdma = (kc + 2) % 3, bnext = (kc + 1) % 3;
+      read_part(P1a, P1b, cur, 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int slot = s & 1;
+        // spread chunk kc+2's DMA over the steps: a VMEM issue stall then overlaps running MFMAs
+        constexpr int kPer = (NSLOT + 5) / 6;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          if (s * kPer + u < NSLOT) issue_slot(kdma, bdma, s * kPer + u);
+        if (s == 3) {
+          read_part(P0a, P0b, bnext, 0);  // P0 of this chunk was last used by step 3's dequant
+          read_scales(bnext);
+        }
+        if (s == 6) cvt_scales(Na, Nb);
+        if (s < 3) deq(P0a, P0b, Ea, Eb, s + 1, slot ^ 1);
+        else if (s < 7) deq(P1a, P1b, Ea, Eb, s + 1, slot ^ 1);
+        else deq(P0a, P0b, Na, Nb, 0, slot ^ 1);
+        mfma_step(slot);
+        interleave();
+        if (s < 6) __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);  // this step's DMA loads
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) { Ea[i][0] = Na[i][0]; Ea[i][1] = Na[i][1]; }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) { Eb[j][0] = Nb[j][0]; Eb[j][1] = Nb[j][1]; }
+    }
+  } else {
+    // ---- W4A16: chunk fragments into registers, next chunk's DMA, 8 pipelined steps ----
+    issue(0, 0);
+    if (Kc > 1) issue(1, 1);
+    wait_vmem();
+    __syncthreads();
+    for (int kc = 0; kc < Kc; ++kc) {
+      const int cur = kc % 3;
+      if (kc > 0) {
+        wait_vmem();
+        __syncthreads();
+      }
+      const uint8_t *st = smem + cur * Cfg::kStage;
+      const uint8_t *sA = st, *sB = st + Cfg::kALds + Cfg::kASLds, *sBS = sB + Cfg::kBLds;
+      u32x4 bc[2][TN];
+      uint32_t bsw[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int unit = wn * (BN / WN / 32) + j;
+        bsw[j] = *reinterpret_cast<const uint32_t *>(sBS + (unit * 64 + lane) * 4);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) bc[p][j] = *reinterpret_cast<const u32x4 *>(sB + ((unit * 2 + p) * 64 + lane) * 16);
+      }
+      if (kc + 2 < Kc) issue(kc + 2, (kc + 2) % 3);
+      float eb[TN][4];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) eb[j][t] = e4m3_to_f32((bsw[j] >> (8 * t)) & 0xffu);
+      bf16x8 bf[2][TN];
+      u32x4 ar[2][TM];
+      auto deq = [&](int s, int slot) {
+        const int p = s >> 2, q = s & 3, blk = s >> 1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[slot][j] = dequant_bf16x8(bc[p][j][q], eb[j][blk]);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const int sub = (wm * (BM / WM)) / 32 + i;
-          ac[i] = *reinterpret_cast<const u32x4 *>(sA + ((sub * 2 + p) * 64 + lane) * 16);
+          const int sub = wm * (BM / WM / 32) + i;
+          ar[slot][i] = *reinterpret_cast<const u32x4 *>(sA + ((sub * 8 + s) * 64 + lane) * 16);
         }
-      }
+      };
+      deq(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s = 4 * p + q;    // MFMA step within the chunk
-        const int blk = s >> 1;     // lane's scale block (of its 4) for this step
-        if (MODE == 0) {
-          f16x8 af[TM], bf[TN];
+      for (int s = 0; s < 8; ++s) {
+        const int slot = s & 1;
+        if (s + 1 < 8) deq(s + 1, slot ^ 1);
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const _Float16 e = (_Float16)e4m3_to_f32((asw[i] >> (8 * blk)) & 0xffu);
-            af[i] = dequant_f16x8(ac[i][q], e);
-          }
+        for (int i = 0; i < TM; ++i) {
+          const bf16x8 afr = __builtin_bit_cast(bf16x8, ar[slot][i]);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const _Float16 e = (_Float16)e4m3_to_f32((bsw[j] >> (8 * blk)) & 0xffu);
-            bf[j] = dequant_f16x8(bc[j][q], e);
-          }
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        } else {
-          bf16x8 af[TM], bf[TN];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int sub = (wm * (BM / WM)) / 32 + i;
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(sA + ((sub * 8 + s) * 64 + lane) * 16);
-            af[i] = __builtin_bit_cast(bf16x8, w);
-          }
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const float e = e4m3_to_f32((bsw[j] >> (8 * blk)) & 0xffu);
-            bf[j] = dequant_bf16x8(bc[j][q], e);
-          }
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bf[slot][j], acc[i][j], 0, 0, 0);
         }
+        if (s + 1 < 8) {
+#pragma unroll
+          for (int t = 0; t < TM * TN; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (18 * TN) / (TM * TN) + 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    if (kc + 1 < Kc) store_chunk(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: scale by S_A * S_B, convert, store ---------------------------------------------
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
+  typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
+  OutT *C = static_cast<OutT *>(c);
+  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int rbase = m0 + wm * (BM / WM) + i * 32 + 4 * lh;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-      if (col >= N) continue;
+      const int col = n0 + wn * (BN / WN) + j * 32 + lr;
+      OutT *pc = C + (int64_t)rbase * ldc + col;
+      if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * (BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < M) store_out<OUT>(c, ldc, row, col, acc[i][j][v] * sab);
+        for (int v = 0; v < 16; ++v) pc[(int64_t)(8 * (v >> 2) + (v & 3)) * ldc] = (OutT)(acc[i][j][v] * sab);
+      } else if (col < N) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rbase + 8 * (v >> 2) + (v & 3);
+          if (row < M) pc[(int64_t)(8 * (v >> 2) + (v & 3)) * ldc] = (OutT)(acc[i][j][v] * sab);
+        }
       }
     }
   }
@@ -357,7 +471,7 @@ static hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
   using Cfg = TileCfg<MODE, BM, BN>;
   const int tm = (int)((g.M + BM - 1) / BM), tn = (int)((g.N + BN - 1) / BN);
   auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT>;
-  const int smem = 2 * Cfg::kStage;
+  const int smem = 3 * Cfg::kStage;
   static bool configured = false;  // per instantiation
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -386,7 +500,7 @@ GemmVariant select_gemm_variant(int mode, int64_t M, int64_t N, int64_t K, int64
   if (mode == 0) {
     if (lda % kChunk != 0) return GemmVariant::Generic;
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    return (t256 >= 240) ? GemmVariant::W4A4_256x256 : GemmVariant::W4A4_128x128;
+    return (t256 >= 128) ? GemmVariant::W4A4_256x256 : GemmVariant::W4A4_128x128;
   }
   return GemmVariant::W4A16_128x256;
 }
