@@ -3,13 +3,15 @@
 A step is the hot path for every linear of the block (qkv 1152->3456, proj 1152->1152,
 fc1 1152->4608, fc2 4608->1152 at M = 4096 tokens): dynamic NVFP4 quantization of the bf16
 activation (amax pass + quantize pass) followed by the W4A4 GEMM with bf16 output.  Weights are
-quantized and prepacked once before timing (offline, as a deployed model would ship them).
-Inputs are seeded synthetic tensors resident in device memory before the timed region.
+quantized and prepacked once before timing (offline, as a deployed model ships them).  Inputs are
+seeded synthetic tensors resident in device memory before the timed region.
 
-Prints one JSON line.  `value` is the block's GEMM work (sum of 2 M N K) divided by the measured
-step time, quantization included.  `roofline` describes the dominant GEMM launch, timed with HIP
-events on the stream the kernels run on.  `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload (a few hundred rows of every linear).
+The step's eight kernel launches are captured once in a HIP graph and replayed, so host launch
+overhead is not part of the measurement; every replay is checked bit-for-bit against an eager run
+first.  Prints one JSON line: `value` is the block's GEMM work (sum of 2 M N K) divided by the
+measured step time (quantization included).  `roofline` describes the dominant GEMM launch, whose
+average duration is measured with HIP events around graph replays of back-to-back launches of that
+kernel on the stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
 """
 import argparse
 import json
@@ -29,8 +31,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="launches per per-kernel timing graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
     return ap.parse_args()
@@ -50,18 +53,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
 
     # ---- setup (untimed): inputs, offline weight prep, outputs, workspaces ----------------------
     layers = []
     for name, x, w in workloads.pixart():
         M, K = x.shape
         N = w.shape[0]
-        xd = x.to(dev)
         wp, ws, wS = nv.nvfp4_quantize(w.to(dev))
         bp = nv.nvfp4_prepack_weight(wp, ws)
         del wp, ws
-        L = dict(name=name, M=M, N=N, K=K, x=xd, bp=bp, wS=wS,
+        L = dict(name=name, M=M, N=N, K=K, x=x.to(dev), bp=bp, wS=wS,
                  packed=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
                  scales=torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
                  S=torch.empty(1, dtype=torch.float32, device=dev),
@@ -74,59 +75,96 @@ def main():
         layers.append(L)
     torch.cuda.synchronize()
 
-    def run_layer(L, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def quantize(L):
         nv.nvfp4_quantize(L["x"], L["S"], static=False, packed=L["packed"], scales=L["scales"],
-                          workspace=L["qws"], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+                          workspace=L["qws"])
+
+    def gemm(L):
         nv.nvfp4_gemm(nv.W4A4, L["packed"], L["scales"], L["S"], L["bp"], L["wS"], L["N"], L["K"],
-                      torch.bfloat16, out=L["y"], workspace=L["gws"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+                      torch.bfloat16, out=L["y"], workspace=L["gws"])
+
+    def step():
+        for L in layers:
+            quantize(L)
+            gemm(L)
 
     for _ in range(args.warmup):
-        for L in layers:
-            run_layer(L)
+        step()
     torch.cuda.synchronize()
+    eager = [L["y"].clone() for L in layers]
 
-    # ---- timed region -------------------------------------------------------------------------------
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    # ---- capture the step; check replays against the eager result -------------------------------
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for L in layers:
+            L["y"].zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for L, ref in zip(layers, eager):
+            if not torch.equal(L["y"], ref):
+                raise RuntimeError(f"graph replay differs from eager result for {L['name']}")
+
+    # ---- timed region: K replays of the step ------------------------------------------------------
+    stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for s in range(args.steps):
-        for li, L in enumerate(layers):
-            run_layer(L, evs[s][li])
+    for _ in range(args.steps):
+        graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-kernel durations: graphs of back-to-back launches of one kernel -----------------------
+    def kernel_us(fn, L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(args.kernel_reps):
+                    fn(L)
+        torch.cuda.synchronize()
+        g.replay()  # warm
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * args.kernel_reps)
 
     flops_step = sum(2.0 * L["M"] * L["N"] * L["K"] for L in layers)
     breakdown = {}
-    for li, L in enumerate(layers):
-        q_ms = sum(evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps)) / args.steps
-        g_ms = sum(evs[s][li][1].elapsed_time(evs[s][li][2]) for s in range(args.steps)) / args.steps
+    for L in layers:
+        q_us = kernel_us(quantize, L)
+        g_us = kernel_us(gemm, L)
         qbytes = L["M"] * L["K"] * (2 + 2 + 0.5625)  # amax read + quantize read + codes/scales write
         flops = 2.0 * L["M"] * L["N"] * L["K"]
         breakdown[L["name"]] = dict(
             M=L["M"], N=L["N"], K=L["K"],
-            quantize_us=round(q_ms * 1e3, 2), quantize_GBps=round(qbytes / (q_ms * 1e-3) / 1e9, 1),
-            gemm_us=round(g_ms * 1e3, 2), gemm_TFLOPs=round(flops / (g_ms * 1e-3) / 1e12, 1),
-            gemm_frac=round(flops / (g_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4))
-    dom = max(breakdown.items(), key=lambda kv: kv[1]["gemm_us"])
-    dom_name, d = dom
+            quantize_us=round(q_us, 2), quantize_GBps=round(qbytes / (q_us * 1e-6) / 1e9, 1),
+            gemm_us=round(g_us, 2), gemm_TFLOPs=round(flops / (g_us * 1e-6) / 1e12, 1),
+            gemm_frac=round(flops / (g_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4))
+    dom_name, d = max(breakdown.items(), key=lambda kv: kv[1]["gemm_us"])
     roofline = dict(bound="mfma", achieved=d["gemm_TFLOPs"], peak=PEAK_FP16_TFLOPS, unit="TFLOP/s",
                     frac=round(d["gemm_TFLOPs"] / PEAK_FP16_TFLOPS, 4), traffic=None,
                     kernel=f"W4A4 GEMM {dom_name} M={d['M']} N={d['N']} K={d['K']}",
-                    algorithmic_flops_per_launch=2 * d["M"] * d["N"] * d["K"])
+                    avg_launch_us=d["gemm_us"], algorithmic_flops_per_launch=2 * d["M"] * d["N"] * d["K"])
     q_total_bytes = sum(L["M"] * L["K"] * 4.5625 for L in layers)
     q_total_us = sum(v["quantize_us"] for v in breakdown.values())
+    g_total_us = sum(v["gemm_us"] for v in breakdown.values())
 
     out = {
         "metric": METRIC,
@@ -142,11 +180,13 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "PixArt-style DiT block linears, W4A4, bf16 in/out", "M": 4096, "hidden": 1152,
-                   "linears": {L["name"]: [L["K"], L["N"]] for L in layers}, "parallelism": "none (1 GPU)"},
+                   "linears": {L["name"]: [L["K"], L["N"]] for L in layers}, "parallelism": "none (1 GPU)",
+                   "timing": "HIP-graph replay of the step"},
         "roofline": roofline,
         "quantize": {"achieved_GBps": round(q_total_bytes / (q_total_us * 1e-6) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
                      "frac": round(q_total_bytes / (q_total_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                      "bytes_per_elem": 4.5625, "note": "dynamic: amax pass + quantize pass"},
+        "gemm_TFLOPs_all_linears": round(flops_step / (g_total_us * 1e-6) / 1e12, 1),
         "breakdown": breakdown,
         "wall_s_timed": round(wall, 4),
     }
@@ -173,7 +213,7 @@ def cpu_baseline(layers, rows):
         x16 = L["x_cpu"].view(torch.int16).numpy().view(np.uint16)
         prep.append((x16, B))
     if rows <= 0:
-        # calibrate: aim for roughly 15 s of oracle work in total
+        # calibrate on 32 rows of the first linear: aim for roughly 15 s of oracle work in total
         x16, B = prep[0]
         t = time.perf_counter()
         S = oracle.tensor_scale(x16)
@@ -181,10 +221,9 @@ def cpu_baseline(layers, rows):
         A, _ = oracle.dequantize(p, s, S, threads=threads)
         oracle.gemm(A, B, threads=threads)
         dt = time.perf_counter() - t
-        f0 = 2.0 * 32 * B.shape[0] * B.shape[1]
-        rate = f0 / max(dt, 1e-6)
+        rate = 2.0 * 32 * B.shape[0] * B.shape[1] / max(dt, 1e-6)
         total_per_row = sum(2.0 * Bx.shape[0] * Bx.shape[1] for _, Bx in prep)
-        rows = int(max(16, min(4096, 15.0 * rate / total_per_row)))
+        rows = int(max(16, min(layers[0]["M"], 15.0 * rate / total_per_row)))
     flops = 0.0
     t = time.perf_counter()
     for x16, B in prep:
@@ -195,8 +234,8 @@ def cpu_baseline(layers, rows):
         flops += 2.0 * rows * B.shape[0] * B.shape[1]
     dt = time.perf_counter() - t
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of 4096 rows of every linear (full-activation tensor scale, quantize, "
-                      f"dequantize, fp64-accumulated GEMM); {dt:.1f} s"}
+            "sample": f"first {rows} of {layers[0]['M']} rows of every linear (full-activation tensor scale, "
+                      f"quantize, dequantize, fp64-accumulated GEMM); {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -84,6 +84,74 @@ __device__ __forceinline__ void g2l4(const void *g, uint8_t *lds) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Output staging.  The MFMAs compute C^T tiles (the B fragment is the row operand), so lane l of
+// 32x32 tile (i, j) holds output row r = l % 32 of the tile and, for g = 0..3, the four consecutive
+// columns 8 g + 4 (l / 32) + 0..3.  Each 32-row slab of a wave's sub-tile is written to a
+// wave-private, padded, row-major LDS region (one 8- or 16-byte write per column group) and read
+// back row-contiguously, so every global store instruction covers whole rows of the sub-tile with
+// 16-byte lane stores.
+template <int CW, int ES>
+struct EpiPitch {
+  static constexpr int kPitch = CW * ES + 16;  // row pitch in bytes (16-B pad against bank conflicts)
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  // LDS accesses of one wave complete in order; this only keeps the compiler from reordering them.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int CW, int TM, int TN, typename OutT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float scale, OutT *__restrict__ C,
+                                           int64_t ldc, int M, int N, int row0, int col0, bool vec,
+                                           uint8_t *lds, int lane) {
+  constexpr int ES = (int)sizeof(OutT);
+  constexpr int kPitch = EpiPitch<CW, ES>::kPitch;
+  constexpr int kLanesPerRow = CW * ES / 16;
+  constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  constexpr int kEl = 16 / ES;  // elements per 16-byte lane access
+  static_assert(CW == 32 * TN && kLanesPerRow <= 64 && 64 % kLanesPerRow == 0, "epilogue shape");
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rr = lane / kLanesPerRow, cq = (lane % kLanesPerRow) * kEl;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float v0 = acc[i][j][4 * g] * scale, v1 = acc[i][j][4 * g + 1] * scale;
+        const float v2 = acc[i][j][4 * g + 2] * scale, v3 = acc[i][j][4 * g + 3] * scale;
+        uint8_t *p = lds + lr * kPitch + (j * 32 + 8 * g + 4 * lh) * ES;
+        if (ES == 4) {
+          const u32x4 o = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+          *reinterpret_cast<u32x4 *>(p) = o;
+        } else {
+          const bf16x2 h0 = {(__bf16)v0, (__bf16)v1}, h1 = {(__bf16)v2, (__bf16)v3};
+          const u32x2 o = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+          *reinterpret_cast<u32x2 *>(p) = o;
+        }
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 32 / kRowsPerRead; ++t) {
+      const int r = t * kRowsPerRead + rr;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r * kPitch + cq * ES);
+      const int row = row0 + i * 32 + r, col = col0 + cq;
+      OutT *pc = C + (int64_t)row * ldc + col;
+      if (vec) {
+        *reinterpret_cast<u32x4 *>(pc) = v;
+      } else if (row < M) {
+        const OutT *e = reinterpret_cast<const OutT *>(&v);
+#pragma unroll
+        for (int q = 0; q < kEl; ++q)
+          if (col + q < N) pc[q] = e[q];
+      }
+    }
+    wave_lds_sync();  // the next slab overwrites this region
+  }
+}
+
 // MODE 0 = W4A4 (fp16 MFMA), 1 = W4A16 (bf16 MFMA).  WM x WN waves of (BM/WM) x (BN/WN).
 //
 // LDS stage layout (one per buffer, two buffers):
@@ -99,7 +167,8 @@ template <int MODE, int BM, int BN, int WM, int WN, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
-    void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n) {
+    void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int m_off, int n_off, int splits,
+    float *__restrict__ partial) {
   using Cfg = TileCfg<MODE, BM, BN>;
   constexpr int TM = BM / WM / 32;  // MFMA tiles per wave along M
   constexpr int TN = BN / WN / 32;
@@ -107,6 +176,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NAS = (MODE == 0) ? BM / 32 : 0;                    // 256-B A scale blocks
   constexpr int NB = (BN / 32) * 2, NBS = BN / 32;
   static_assert(NA % 4 == 0 && NB % 4 == 0 && NBS % 4 == 0 && NAS % 4 == 0, "block counts");
+  static_assert(4 * 32 * EpiPitch<BN / WN, 4>::kPitch <= 3 * Cfg::kStage, "epilogue staging fits the LDS ring");
   constexpr int kAStep = (MODE == 0) ? 64 : 256;  // A bytes per row per chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -116,87 +186,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // XCD-aware tile order: consecutive dispatches land on different XCDs; give each XCD a
   // contiguous range of tiles (row-major over the tile grid) so its L2 sees shared A rows.
+  // Split-K: workgroup = (tile, split); split s covers chunks [s Kc / splits, (s+1) Kc / splits).
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   {
-    const int full = (ntiles / 8) * 8;  // bijective remap on the multiple-of-8 prefix
+    const int nwg = ntiles * splits;
+    const int full = (nwg / 8) * 8;  // bijective remap on the multiple-of-8 prefix
     if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
   }
+  const int split = bid / ntiles;
+  bid -= split * ntiles;
   const int tile_m = bid / tiles_n, tile_n = bid % tiles_n;
-  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int m0 = m_off + tile_m * BM, n0 = n_off + tile_n * BN;
 
   const int Kc = K / kChunk;
+  const int kbeg = (int)((int64_t)split * Kc / splits), kend = (int)((int64_t)(split + 1) * Kc / splits);
   const int Nu = (N + 31) / 32;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
   const int lh = lane >> 5, lr = lane & 31;
 
-  // ---- per-lane source addresses of this wave's LDS-DMA loads (chunk 0) -------------------------
-  const uint8_t *pa[NA / 4];
-  const uint8_t *pas[NAS / 4 > 0 ? NAS / 4 : 1];
-  const uint8_t *pb[NB / 4];
-  const uint8_t *pbs[NBS / 4];
+  // ---- sources of this wave's LDS-DMA loads: wave-uniform bases (SGPRs) + 32-bit lane offsets ----
+  // A rows past M are clamped to M - 1 and B units past N to the last unit (results never stored).
+  // The host guarantees BM * (A row bytes) < 2^31, so the A lane offsets fit in 32 bits.
+  const int64_t arow_bytes = (MODE == 0) ? lda / 2 : lda * 2;
+  const uint8_t *a_tile = static_cast<const uint8_t *>(a) + (int64_t)m0 * arow_bytes;
+  const uint8_t *as_tile = (MODE == 0) ? a_scales + (int64_t)m0 * (lda / 16) : nullptr;
+  uint32_t oa[NA / 4];
+  uint32_t oas[NAS / 4 > 0 ? NAS / 4 : 1];
 #pragma unroll
   for (int i = 0; i < NA / 4; ++i) {
     const int q = wave + 4 * i;
     if (MODE == 0) {
       const int sub = q >> 1, part = q & 1;
-      const int row = min(m0 + sub * 32 + lr, M - 1);
-      pa[i] = static_cast<const uint8_t *>(a) + (int64_t)row * (lda / 2) + 32 * lh + 16 * part;
+      const int row = min(m0 + sub * 32 + lr, M - 1) - m0;
+      oa[i] = (uint32_t)(row * (uint32_t)arow_bytes) + 32 * lh + 16 * part;
     } else {
       const int sub = q >> 3, st = q & 7;
-      const int row = min(m0 + sub * 32 + lr, M - 1);
-      pa[i] = reinterpret_cast<const uint8_t *>(static_cast<const uint16_t *>(a) + (int64_t)row * lda + 64 * lh + 8 * st);
+      const int row = min(m0 + sub * 32 + lr, M - 1) - m0;
+      oa[i] = (uint32_t)(row * (uint32_t)arow_bytes) + 2 * (64 * lh + 8 * st);
     }
   }
 #pragma unroll
   for (int i = 0; i < NAS / 4; ++i) {
     const int q = wave + 4 * i;
-    const int row = min(m0 + q * 32 + lr, M - 1);
-    pas[i] = a_scales + (int64_t)row * (lda / 16) + 4 * lh;
+    const int row = min(m0 + q * 32 + lr, M - 1) - m0;
+    oas[i] = (uint32_t)(row * (uint32_t)(lda / 16)) + 4 * lh;
   }
-#pragma unroll
-  for (int i = 0; i < NB / 4; ++i) {
-    const int q = wave + 4 * i;
-    const int nu = min(n0 / 32 + (q >> 1), Nu - 1);
-    pb[i] = bp + (uint64_t)nu * (uint64_t)Kc * 2048ull + (q & 1) * 1024 + lane * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < NBS / 4; ++i) {
-    const int q = wave + 4 * i;
+  const uint32_t ob = lane * 16, obs = lane * 4;
+  // prepacked B unit (n-unit nu, chunk kc) of this wave's q-th block
+  auto b_unit = [&](int q, int kc) -> uint64_t {
     const int nu = min(n0 / 32 + q, Nu - 1);
-    pbs[i] = bp + scale_region + (uint64_t)nu * (uint64_t)Kc * 256ull + lane * 4;
-  }
-
-  auto issue = [&](int kc, int buf) {
-    uint8_t *st = smem + buf * Cfg::kStage;
-#pragma unroll
-    for (int i = 0; i < NA / 4; ++i) g2l16(pa[i] + (int64_t)kc * kAStep, st + (wave + 4 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < NAS / 4; ++i) g2l4(pas[i] + kc * 8, st + Cfg::kALds + (wave + 4 * i) * 256);
-#pragma unroll
-    for (int i = 0; i < NB / 4; ++i)
-      g2l16(pb[i] + (int64_t)kc * 2048, st + Cfg::kALds + Cfg::kASLds + (wave + 4 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < NBS / 4; ++i)
-      g2l4(pbs[i] + (int64_t)kc * 256, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (wave + 4 * i) * 256);
+    return ((uint64_t)nu * (uint64_t)Kc + (uint64_t)kc);
   };
 
-  // One of this wave's NSLOT DMA loads of chunk kc (t is a compile-time slot index).
-  constexpr int NSLOT = NA / 4 + NAS / 4 + NB / 4 + NBS / 4;
   auto issue_slot = [&](int kc, int buf, int t) {
     uint8_t *st = smem + buf * Cfg::kStage;
     if (t < NA / 4) {
-      g2l16(pa[t] + (int64_t)kc * kAStep, st + (wave + 4 * t) * 1024);
+      g2l16(a_tile + (int64_t)kc * kAStep + oa[t], st + (wave + 4 * t) * 1024);
     } else if (t < NA / 4 + NAS / 4) {
       const int i = t - NA / 4;
-      g2l4(pas[i] + kc * 8, st + Cfg::kALds + (wave + 4 * i) * 256);
+      g2l4(as_tile + kc * 8 + oas[i], st + Cfg::kALds + (wave + 4 * i) * 256);
     } else if (t < NA / 4 + NAS / 4 + NB / 4) {
-      const int i = t - NA / 4 - NAS / 4;
-      g2l16(pb[i] + (int64_t)kc * 2048, st + Cfg::kALds + Cfg::kASLds + (wave + 4 * i) * 1024);
+      const int i = t - NA / 4 - NAS / 4, q = wave + 4 * i;
+      g2l16(bp + b_unit(q >> 1, kc) * 2048ull + (q & 1) * 1024 + ob,
+            st + Cfg::kALds + Cfg::kASLds + q * 1024);
     } else {
-      const int i = t - NA / 4 - NAS / 4 - NB / 4;
-      g2l4(pbs[i] + (int64_t)kc * 256, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (wave + 4 * i) * 256);
+      const int i = t - NA / 4 - NAS / 4 - NB / 4, q = wave + 4 * i;
+      g2l4(bp + scale_region + b_unit(q, kc) * 256ull + obs, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + q * 256);
     }
+  };
+  constexpr int NSLOT = NA / 4 + NAS / 4 + NB / 4 + NBS / 4;
+  auto issue = [&](int kc, int buf) {
+#pragma unroll
+    for (int t = 0; t < NSLOT; ++t) issue_slot(kc, buf, t);
   };
 
   f32x16 acc[TM][TN];
@@ -207,7 +269,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (MODE == 0) {
+  if (kend <= kbeg) {
+    // empty K range (not produced by the planner): leave the accumulators at zero
+  } else if (MODE == 0) {
     // ---- W4A4: one continuous stream of 16-k steps.  Step s+1 is dequantized while step s's 16
     // MFMAs run (also across chunk boundaries).  Codes are held per half-chunk ("part", 4 steps):
     // part 1 of chunk kc is read at the start of chunk kc, part 0 of chunk kc+1 (and its scales) at
@@ -270,7 +334,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Fa[slot][i], Fb[slot][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Fb[slot][j], Fa[slot][i], acc[i][j], 0, 0, 0);
     };
     auto interleave = [&]() {
 #pragma unroll
@@ -280,8 +344,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
-    issue(0, 0);
-    if (Kc > 1) issue(1, 1);
+    const int nk = kend - kbeg;
+    issue(kbeg, 0);
+    if (nk > 1) issue(kbeg + 1, 1);
     wait_vmem();
     __syncthreads();
     read_part(P0a, P0b, 0, 0);
@@ -290,7 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     deq(P0a, P0b, Ea, Eb, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int kc = 0; kc < Kc; ++kc) {
+    for (int kc = 0; kc < nk; ++kc) {
       const int cur = kc % 3;
       if (kc > 0) {
         wait_vmem();  // this wave's DMA of chunk kc+1 (issued one chunk ago) has landed
@@ -299,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // Branch-free steps (a branch would split the scheduling region): near the end of K the
       // DMA re-fetches the last chunk into the free stage and the look-ahead reads/dequantizes a
       // stale stage; neither result is used.
-      const int kdma = min(kc + 2, Kc - 1);
+      const int kdma = kbeg + min(kc + 2, nk - 1);
       const int bdma = (kc + 2) % 3, bnext = (kc + 1) % 3;
       read_part(P1a, P1b, cur, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -331,11 +396,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   } else {
     // ---- W4A16: chunk fragments into registers, next chunk's DMA, 8 pipelined steps ----
-    issue(0, 0);
-    if (Kc > 1) issue(1, 1);
+    const int nk = kend - kbeg;
+    issue(kbeg, 0);
+    if (nk > 1) issue(kbeg + 1, 1);
     wait_vmem();
     __syncthreads();
-    for (int kc = 0; kc < Kc; ++kc) {
+    for (int kc = 0; kc < nk; ++kc) {
       const int cur = kc % 3;
       if (kc > 0) {
         wait_vmem();
@@ -352,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int p = 0; p < 2; ++p) bc[p][j] = *reinterpret_cast<const u32x4 *>(sB + ((unit * 2 + p) * 64 + lane) * 16);
       }
-      if (kc + 2 < Kc) issue(kc + 2, (kc + 2) % 3);
+      if (kc + 2 < nk) issue(kbeg + kc + 2, (kc + 2) % 3);
       float eb[TN][4];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -381,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const bf16x8 afr = __builtin_bit_cast(bf16x8, ar[slot][i]);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bf[slot][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[slot][j], afr, acc[i][j], 0, 0, 0);
         }
         if (s + 1 < 8) {
 #pragma unroll
@@ -396,29 +462,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- epilogue: scale by S_A * S_B, convert, store ---------------------------------------------
+  __syncthreads();  // every wave is done reading the LDS ring; it now stages output
+  uint8_t *lds_wave = smem + wave * (32 * EpiPitch<BN / WN, 4>::kPitch);
+  const int row0 = m0 + wm * (BM / WM), col0 = n0 + wn * (BN / WN);
+  if (splits > 1) {
+    // unscaled fp32 partial tile -> partial[split][M][N]; the reduce kernel scales and converts
+    const bool vec = (m0 + BM <= M) && (n0 + BN <= N) && (N % 4 == 0);
+    store_tile<BN / WN, TM, TN, float>(acc, 1.0f, partial + (int64_t)split * M * N, N, M, N, row0, col0, vec,
+                                       lds_wave, lane);
+    return;
+  }
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
   typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
-  OutT *C = static_cast<OutT *>(c);
-  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int rbase = m0 + wm * (BM / WM) + i * 32 + 4 * lh;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * (BN / WN) + j * 32 + lr;
-      OutT *pc = C + (int64_t)rbase * ldc + col;
-      if (full) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) pc[(int64_t)(8 * (v >> 2) + (v & 3)) * ldc] = (OutT)(acc[i][j][v] * sab);
-      } else if (col < N) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + 8 * (v >> 2) + (v & 3);
-          if (row < M) pc[(int64_t)(8 * (v >> 2) + (v & 3)) * ldc] = (OutT)(acc[i][j][v] * sab);
-        }
-      }
-    }
-  }
+  const bool vec = (m0 + BM <= M) && (n0 + BN <= N) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+  store_tile<BN / WN, TM, TN, OutT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec, lds_wave, lane);
 }
 
 // ---- generic fallback (any K % 16 == 0): one thread per output element ---------------------------
@@ -464,12 +521,56 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const void *__restrict__ a
   }
 }
 
+// ---- split-K reduction: C = (sum over splits, in order) * S_A S_B, deterministic ----------------
+
+template <int OUT>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial, int splits, int M, int N,
+                                                       void *__restrict__ c, int64_t ldc, const float *__restrict__ a_ts,
+                                                       const float *__restrict__ b_ts) {
+  const float sab = a_ts ? (*a_ts) * (*b_ts) : *b_ts;
+  const int64_t MN = (int64_t)M * N;
+  const bool vec = (ldc % 4 == 0);  // 4-element stores stay aligned (c is 16-byte aligned)
+  const int64_t nq = MN / 4;  // N % 4 == 0 here
+  for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < nq; q += (int64_t)gridDim.x * 256) {
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + 4 * q);
+    for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4 *>(partial + sp * MN + 4 * q);
+    const int64_t m = (4 * q) / N, n = (4 * q) % N;
+    acc *= sab;
+    if (OUT == 0) {
+      float *dst = static_cast<float *>(c) + m * ldc + n;
+      if (vec) {
+        *reinterpret_cast<f32x4 *>(dst) = acc;
+      } else {
+        dst[0] = acc.x;
+        dst[1] = acc.y;
+        dst[2] = acc.z;
+        dst[3] = acc.w;
+      }
+    } else {
+      __bf16 *dst = static_cast<__bf16 *>(c) + m * ldc + n;
+      if (vec) {
+        const bf16x2 h0 = {(__bf16)acc.x, (__bf16)acc.y}, h1 = {(__bf16)acc.z, (__bf16)acc.w};
+        u32x2 o;
+        o.x = __builtin_bit_cast(uint32_t, h0);
+        o.y = __builtin_bit_cast(uint32_t, h1);
+        *reinterpret_cast<u32x2 *>(dst) = o;
+      } else {
+        dst[0] = (__bf16)acc.x;
+        dst[1] = (__bf16)acc.y;
+        dst[2] = (__bf16)acc.z;
+        dst[3] = (__bf16)acc.w;
+      }
+    }
+  }
+}
+
 // ---- launchers ----------------------------------------------------------------------------------
 
 template <int MODE, int BM, int BN, int WM, int WN, int OUT>
-static hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
+static hipError_t launch_tiled(const GemmArgs &g, int m_off, int n_off, int m_len, int n_len, int splits,
+                               float *partial, hipStream_t stream) {
   using Cfg = TileCfg<MODE, BM, BN>;
-  const int tm = (int)((g.M + BM - 1) / BM), tn = (int)((g.N + BN - 1) / BN);
+  const int tm = (m_len + BM - 1) / BM, tn = (n_len + BN - 1) / BN;
   auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT>;
   const int smem = 3 * Cfg::kStage;
   static bool configured = false;  // per instantiation
@@ -479,8 +580,9 @@ static hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  kern<<<tm * tn, 256, smem, stream>>>(g.a, g.a_scales, g.a_ts, static_cast<const uint8_t *>(g.b), g.b_ts,
-                                       (int)g.M, (int)g.N, (int)g.K, g.lda, g.c, g.ldc, tm, tn);
+  kern<<<tm * tn * splits, 256, smem, stream>>>(g.a, g.a_scales, g.a_ts, static_cast<const uint8_t *>(g.b), g.b_ts,
+                                                (int)g.M, (int)g.N, (int)g.K, g.lda, g.c, g.ldc, tm, tn, m_off, n_off,
+                                                splits, partial);
   return hipGetLastError();
 }
 
@@ -495,35 +597,87 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-GemmVariant select_gemm_variant(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
-  if (K % kChunk != 0) return GemmVariant::Generic;
-  if (mode == 0) {
-    if (lda % kChunk != 0) return GemmVariant::Generic;
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    return (t256 >= 128) ? GemmVariant::W4A4_256x256 : GemmVariant::W4A4_128x128;
+// Plan: which tile kernel(s), how many K splits, and an optional split of N into a region of
+// 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
+GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
+  GemmPlan pl;
+  const int64_t arow_bytes = (mode == 0) ? lda / 2 : lda * 2;
+  if (K % kChunk != 0 || (mode == 0 && lda % kChunk != 0) || 256 * arow_bytes >= (int64_t(1) << 31)) {
+    // the tiled kernels need whole 128-k chunks and 32-bit A offsets within a 256-row tile
+    pl.variant = GemmVariant::Generic;
+    return pl;
   }
-  return GemmVariant::W4A16_128x256;
+  const int64_t cus = 256;  // planning for the MI355X chip (one workgroup of either tile per CU)
+  const int64_t Kc = K / kChunk;
+  if (mode == 1) {
+    pl.variant = GemmVariant::W4A16_128x256;
+    return pl;
+  }
+  const int64_t tmb = (M + 255) / 256, tnb = (N + 255) / 256, tb = tmb * tnb;
+  pl.variant = GemmVariant::W4A4_256x256;
+  if (tb >= cus) {
+    // more than one round: cover whole big-tile rounds, finish the rest with 128x128 tiles
+    const int64_t cols = cus / tmb;  // big-tile columns that make exactly one round
+    if (cols >= 1 && cols < tnb && N % 128 == 0) {
+      const int64_t rest = ((M + 127) / 128) * ((N - cols * 256 + 127) / 128);  // 128x128 remainder tiles
+      if (rest <= cus) pl.n_big = cols * 256;
+    }
+    return pl;
+  }
+  // fewer tiles than CUs: split K over idle CUs when every split keeps >= 8 chunks
+  int best = 1;
+  for (int sp = 2; sp <= 4; ++sp)
+    if (tb * sp <= cus && Kc / sp >= 8 && N % 4 == 0) best = sp;  // long K only: partials cost HBM traffic
+  if (tb * 2 > cus) best = 1;  // already more than half the chip: a reduction costs more than it saves
+  pl.splits = best;
+  if (best == 1 && tb * 2 <= cus && (M + 127) / 128 * ((N + 127) / 128) <= 2 * cus)
+    pl.variant = GemmVariant::W4A4_128x128;  // small problem with short K: more, smaller tiles
+  return pl;
+}
+
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
+  const GemmPlan pl = plan_gemm(mode, M, N, K, mode == 0 ? K : K);
+  return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int OUT>
+static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t stream) {
+  const int M = (int)g.M, N = (int)g.N;
+  switch (pl.variant) {
+    case GemmVariant::W4A4_256x256: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        int64_t grid = ((int64_t)M * N / 4 + 255) / 256;
+        if (grid > 8192) grid = 8192;
+        k_splitk_reduce<OUT><<<(unsigned)grid, 256, 0, stream>>>(part, pl.splits, M, N, g.c, g.ldc, g.a_ts, g.b_ts);
+        return hipGetLastError();
+      }
+      if (pl.n_big > 0 && pl.n_big < N) {
+        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, (int)pl.n_big, 1, nullptr, stream);
+        if (e != hipSuccess) return e;
+        return launch_tiled<0, 128, 128, 2, 2, OUT>(g, 0, (int)pl.n_big, M, N - (int)pl.n_big, 1, nullptr, stream);
+      }
+      return launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
+    case GemmVariant::W4A4_128x128:
+      return launch_tiled<0, 128, 128, 2, 2, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    case GemmVariant::W4A16_128x256:
+      return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    case GemmVariant::Generic:
+    default:
+      return launch_generic<0, OUT>(g, stream);  // replaced below for W4A16
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
-  const GemmVariant v = select_gemm_variant(g.mode, g.M, g.N, g.K, g.lda);
-  const bool f32 = (g.out_dtype == 0);
-  switch (v) {
-    case GemmVariant::W4A4_256x256:
-      return f32 ? launch_tiled<0, 256, 256, 2, 2, 0>(g, stream) : launch_tiled<0, 256, 256, 2, 2, 1>(g, stream);
-    case GemmVariant::W4A4_128x128:
-      return f32 ? launch_tiled<0, 128, 128, 2, 2, 0>(g, stream) : launch_tiled<0, 128, 128, 2, 2, 1>(g, stream);
-    case GemmVariant::W4A16_128x256:
-      return f32 ? launch_tiled<1, 128, 256, 1, 4, 0>(g, stream) : launch_tiled<1, 128, 256, 1, 4, 1>(g, stream);
-    case GemmVariant::Generic:
-    default:
-      if (g.mode == 0) return f32 ? launch_generic<0, 0>(g, stream) : launch_generic<0, 1>(g, stream);
-      return f32 ? launch_generic<1, 0>(g, stream) : launch_generic<1, 1>(g, stream);
+  const GemmPlan pl = plan_gemm(g.mode, g.M, g.N, g.K, g.lda);
+  if (pl.variant == GemmVariant::Generic) {
+    if (g.mode == 0) return g.out_dtype == 0 ? launch_generic<0, 0>(g, stream) : launch_generic<0, 1>(g, stream);
+    return g.out_dtype == 0 ? launch_generic<1, 0>(g, stream) : launch_generic<1, 1>(g, stream);
   }
+  return g.out_dtype == 0 ? run_plan<0>(g, pl, stream) : run_plan<1>(g, pl, stream);
 }
 
-}  // namespace nvfp4
-
-namespace nvfp4 {
-size_t gemm_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 }  // namespace nvfp4

@@ -21,6 +21,12 @@ hipError_t launch_unpack(const void *in, int64_t N, int64_t K, uint8_t *packed, 
 
 enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256 };
 
+struct GemmPlan {
+  GemmVariant variant = GemmVariant::Generic;
+  int splits = 1;     // K splits (partial tiles reduced by a second kernel)
+  int64_t n_big = 0;  // > 0: columns [0, n_big) in 256x256 tiles, the rest in 128x128 tiles
+};
+
 struct GemmArgs {
   int mode;  // 0 W4A4, 1 W4A16
   const void *a;
@@ -35,7 +41,7 @@ struct GemmArgs {
   void *workspace;
 };
 
-GemmVariant select_gemm_variant(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
+GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 

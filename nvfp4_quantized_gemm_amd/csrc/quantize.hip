@@ -11,19 +11,22 @@
 // Dynamic mode runs k_amax first (per-workgroup partial maxima, no atomics, deterministic); every
 // quantize workgroup reduces those partials itself and derives S = RN32(amax / 2688).
 //
-// Exactness.  Block scale: r = amax / (6 S) is computed as one fp64 division.  The exact quotient
-// differs from any E4M3 midpoint (<= 5 significant bits) by at least 2^-31 relative unless it
-// equals it, because amax has 24 and 6 S has 26 significant bits; the fp64 rounding (2^-53) can
-// therefore neither cross nor create a midpoint, and rint() on the scaled fp64 value is the exact
-// round-half-even decision.
-// Element codes, fast path: with inv = 1/(e S) in fp64, lo = RN32(inv (1 - 2^-21)) and
-// hi = RN32(inv (1 + 2^-21)) bracket it; the fp32 products v*lo and v*hi then bracket the exact
-// quotient v/(e S) strictly (three roundings of 2^-24 cannot undo a 2^-21 margin).  The hardware
-// E2M1 conversion (round-half-even, saturating, sign-preserving) is monotone, so when the two
-// bracketing codes agree that code is the exact one.  A block in which any pair disagrees (a
-// value within ~2^-20 of a decision boundary, e.g. an exact tie) takes the exact path: seven
-// per-block fp32 thresholds U_k obtained from the exact fp64 boundaries t_k e S by directed
-// rounding, code = #{k : |v| >= U_k}.
+// Exactness (all fast paths bracket the exact real quotient and fall back when unsure):
+//  * Block scale.  With c = 1/(6 S) (fp64, once per workgroup), rl = RN32(amax RN32(c (1 - 2^-20)))
+//    and rh = RN32(amax RN32(c (1 + 2^-20))) satisfy rl < amax / (6 S) < rh (a few 2^-24 roundings
+//    cannot undo a 2^-20 margin).  The hardware fp32 -> E4M3 conversion rounds to nearest-even and
+//    is monotone; after clamping to 448 (saturation) the bytes of rl and rh are equal unless the
+//    exact ratio lies within ~2^-19 of a midpoint, and then that common byte is the exact one.
+//    Otherwise scale_byte_exact() decides with one fp64 division: the exact quotient differs from
+//    any E4M3 midpoint (<= 5 significant bits) by >= 2^-31 relative unless equal to it (amax has 24
+//    and 6 S 26 significant bits), so the fp64 rounding (2^-53) neither crosses nor creates one.
+//  * Element codes.  inv = rcp(e) * RN32(1/S) is within 3 ulp of 1/(e S); lo = RN32(inv (1 - 2^-20))
+//    and hi = RN32(inv (1 + 2^-20)) make the fp32 products v*lo and v*hi bracket v/(e S) strictly.
+//    The hardware E2M1 conversion (round-half-even, saturating, sign-preserving) is monotone, so
+//    when the two bracketing codes agree that code is the exact one.  A block in which any pair
+//    disagrees (a value within ~2^-19 of a decision boundary, e.g. an exact tie) takes the exact
+//    path: seven per-block fp32 thresholds U_k from the exact fp64 boundaries t_k e S by directed
+//    rounding, code = #{k : |v| >= U_k}.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -100,7 +103,7 @@ __device__ __forceinline__ float ru32(double d) {
 // Exact code magnitudes through per-block thresholds.  Boundaries between consecutive E2M1 grid
 // values at t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}; a tie rounds to the even code, i.e. down at
 // 0.25, 1.25, 2.5, 5 and up at 0.75, 1.75, 3.5.  U_k is the least fp32 value whose code is >= k.
-__device__ __noinline__ void codes_exact(const float v[16], float e, float S, uint32_t &w0, uint32_t &w1) {
+__device__ __forceinline__ void codes_exact(const float v[16], float e, float S, uint32_t &w0, uint32_t &w1) {
   const double es = (double)e * (double)S;  // exact: 4 x 24 significant bits
   float U[7];
   U[0] = next_up(rd32(0.25 * es));
@@ -130,13 +133,20 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_t ld, uint32_t nblk,
                                               FastDiv bpr, float *__restrict__ partial) {
   float m = 0.0f;
-  for (uint32_t b = blockIdx.x * 256u + threadIdx.x; b < nblk; b += gridDim.x * 256u) {
-    uint32_t row = fastdiv(b, bpr);
-    uint32_t col = b - row * bpr.d;
-    float v[16];
-    BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v);
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t b0 = blockIdx.x * 256u + threadIdx.x; b0 < nblk; b0 += 4 * stride) {
+    float v[4][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < 4; ++u) {  // four blocks' loads in flight per thread
+      const uint32_t b = (b0 + u * stride < nblk) ? b0 + u * stride : b0;
+      const uint32_t row = fastdiv(b, bpr);
+      const uint32_t col = b - row * bpr.d;
+      BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[u][i]));
   }
   // workgroup reduction
 #pragma unroll
@@ -175,55 +185,79 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   __syncthreads();
   const float S = s_S;
   const bool fast_ok = (S >= kFastSMin) && (S <= kFastSMax);
+  // per-workgroup constants of the bracketing fast paths
+  const double c6 = fast_ok ? 1.0 / (6.0 * (double)S) : 0.0;
+  const float rlo = (float)(c6 * (1.0 - 0x1p-20)), rhi = (float)(c6 * (1.0 + 0x1p-20));
+  const float invS = fast_ok ? (float)(1.0 / (double)S) : 0.0f;
 
-  for (uint32_t b = blockIdx.x * 256u + threadIdx.x; b < nblk; b += gridDim.x * 256u) {
-    uint32_t row = fastdiv(b, bpr);
-    uint32_t col = b - row * bpr.d;
-    float v[16];
-    BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v);
-    float amax = 0.0f;
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t b0 = blockIdx.x * 256u + threadIdx.x; b0 < nblk; b0 += 2 * stride) {
+    // two blocks per thread per iteration: both loads are in flight before any compute
+    const uint32_t bb[2] = {b0, b0 + stride};
+    float v[2][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-
-    uint32_t byte = 0, w0 = 0, w1 = 0;
-    if (amax > 0.0f) byte = scale_byte_exact(amax, S);
-    if (byte == 0) {
-      // zero or flushed block: magnitude 0, sign copied
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t sgn = (__float_as_uint(v[i]) >> 28) & 8u;
-        if (i < 8) w0 |= sgn << (4 * i);
-        else w1 |= sgn << (4 * (i - 8));
-      }
-    } else {
-      const float e = e4m3_to_f32(byte);
-      bool exact = !fast_ok;
-      if (fast_ok) {
-        const double inv = 1.0 / ((double)e * (double)S);
-        const float ilo = (float)(inv * (1.0 - 0x1p-21));
-        const float ihi = (float)(inv * (1.0 + 0x1p-21));
-        uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
-#define NVFP4_ENC(J)                                                 \
-  l0 = fp4_encode2<J>(l0, v[2 * J] * ilo, v[2 * J + 1] * ilo);       \
-  h0 = fp4_encode2<J>(h0, v[2 * J] * ihi, v[2 * J + 1] * ihi);       \
-  l1 = fp4_encode2<J>(l1, v[8 + 2 * J] * ilo, v[9 + 2 * J] * ilo);   \
-  h1 = fp4_encode2<J>(h1, v[8 + 2 * J] * ihi, v[9 + 2 * J] * ihi);
-        NVFP4_ENC(0)
-        NVFP4_ENC(1)
-        NVFP4_ENC(2)
-        NVFP4_ENC(3)
-#undef NVFP4_ENC
-        w0 = l0;
-        w1 = l1;
-        exact = (l0 != h0) || (l1 != h1);
-      }
-      if (exact) codes_exact(v, e, S, w0, w1);
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t b = bb[u] < nblk ? bb[u] : b0;
+      const uint32_t row = fastdiv(b, bpr);
+      const uint32_t col = b - row * bpr.d;
+      BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v[u]);
     }
-    u32x2 o;
-    o.x = w0;
-    o.y = w1;
-    *reinterpret_cast<u32x2 *>(packed + 8ull * b) = o;
-    scales[b] = (uint8_t)byte;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t b = bb[u];
+      if (b >= nblk) break;
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+
+      uint32_t byte = 0, w0 = 0, w1 = 0;
+      if (amax > 0.0f) {
+        if (fast_ok) {
+          const float ra = fminf(amax * rlo, kE4M3Max), rb = fminf(amax * rhi, kE4M3Max);
+          const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
+          byte = pk & 0xffu;
+          if (byte != ((pk >> 8) & 0xffu)) byte = scale_byte_exact(amax, S);
+        } else {
+          byte = scale_byte_exact(amax, S);
+        }
+      }
+      if (byte == 0) {
+        // zero or flushed block: magnitude 0, sign copied
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t sgn = (__float_as_uint(v[u][i]) >> 28) & 8u;
+          if (i < 8) w0 |= sgn << (4 * i);
+          else w1 |= sgn << (4 * (i - 8));
+        }
+      } else {
+        const float e = e4m3_to_f32(byte);
+        bool exact = !fast_ok;
+        if (fast_ok) {
+          const float inv = __builtin_amdgcn_rcpf(e) * invS;
+          const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
+          uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
+#define NVFP4_ENC(J)                                                              \
+  l0 = fp4_encode2<J>(l0, v[u][2 * J] * ilo, v[u][2 * J + 1] * ilo);             \
+  h0 = fp4_encode2<J>(h0, v[u][2 * J] * ihi, v[u][2 * J + 1] * ihi);             \
+  l1 = fp4_encode2<J>(l1, v[u][8 + 2 * J] * ilo, v[u][9 + 2 * J] * ilo);         \
+  h1 = fp4_encode2<J>(h1, v[u][8 + 2 * J] * ihi, v[u][9 + 2 * J] * ihi);
+          NVFP4_ENC(0)
+          NVFP4_ENC(1)
+          NVFP4_ENC(2)
+          NVFP4_ENC(3)
+#undef NVFP4_ENC
+          w0 = l0;
+          w1 = l1;
+          exact = (l0 != h0) || (l1 != h1);
+        }
+        if (exact) codes_exact(v[u], e, S, w0, w1);
+      }
+      u32x2 o;
+      o.x = w0;
+      o.y = w1;
+      *reinterpret_cast<u32x2 *>(packed + 8ull * b) = o;
+      scales[b] = (uint8_t)byte;
+    }
   }
 }
 
