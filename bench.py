@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per per-kernel timing graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernel section")
+    ap.add_argument("--kernel-probe", action="store_true",
+                    help="only launch the dominant GEMM call and a 256 MiB device copy, --steps times each "
+                         "(the workload of the rocprofv3 counter passes)")
     return ap.parse_args()
 
 
@@ -87,6 +91,12 @@ def main():
         for L in layers:
             quantize(L)
             gemm(L)
+
+    if args.kernel_probe:
+        for L in layers:
+            quantize(L)
+        kernel_probe(args, layers, gemm)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -157,11 +167,17 @@ def main():
             quantize_us=round(q_us, 2), quantize_GBps=round(qbytes / (q_us * 1e-6) / 1e9, 1),
             gemm_us=round(g_us, 2), gemm_TFLOPs=round(flops / (g_us * 1e-6) / 1e12, 1),
             gemm_frac=round(flops / (g_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4))
-    dom_name, d = max(breakdown.items(), key=lambda kv: kv[1]["gemm_us"])
+    d = breakdown[DOMINANT]
+    traffic = measured_traffic()
     roofline = dict(bound="mfma", achieved=d["gemm_TFLOPs"], peak=PEAK_FP16_TFLOPS, unit="TFLOP/s",
-                    frac=round(d["gemm_TFLOPs"] / PEAK_FP16_TFLOPS, 4), traffic=None,
-                    kernel=f"W4A4 GEMM {dom_name} M={d['M']} N={d['N']} K={d['K']}",
-                    avg_launch_us=d["gemm_us"], algorithmic_flops_per_launch=2 * d["M"] * d["N"] * d["K"])
+                    frac=round(d["gemm_TFLOPs"] / PEAK_FP16_TFLOPS, 4),
+                    traffic=None if traffic is None else int(traffic),
+                    kernel=f"nvfp4_gemm W4A4 {DOMINANT} M={d['M']} N={d['N']} K={d['K']} bf16 out "
+                           f"(launches: {gemm_kernels(nv, d)})",
+                    avg_launch_us=d["gemm_us"], algorithmic_flops_per_launch=2 * d["M"] * d["N"] * d["K"],
+                    algorithmic_bytes_per_launch=int(d["M"] * d["K"] * 0.5625 + d["N"] * d["K"] * 0.5625
+                                                     + d["M"] * d["N"] * 2),
+                    kernel_source_sha256=kernel_source_hash())
     q_total_bytes = sum(L["M"] * L["K"] * 4.5625 for L in layers)
     q_total_us = sum(v["quantize_us"] for v in breakdown.values())
     g_total_us = sum(v["gemm_us"] for v in breakdown.values())
@@ -190,9 +206,146 @@ def main():
         "breakdown": breakdown,
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_hbm:
+        out["hbm_kernels"] = hbm_kernels(side, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+DOMINANT = "fc2"  # the block's longest GEMM call (4608 -> 1152)
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fc2_traffic.json")
+KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp")
+
+
+def gemm_kernels(nv, d):
+    """The kernels one call launches at this shape (the split-K plan needs a workspace)."""
+    ws = nv.nvfp4_gemm_workspace_bytes(nv.W4A4, d["M"], d["N"], d["K"])
+    if ws:
+        return f"k_gemm_tiled 256x256 split-K x{ws // (4 * d['M'] * d['N'])} + k_splitk_reduce"
+    return "k_gemm_tiled"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nvfp4_quantized_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per call of the dominant GEMM from the committed counter passes, scaled by the
+    counters' reading for a plain copy of known size; None if the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t["fetch_bytes_per_call"] / t["copy_fetch_factor"] + t["write_bytes_per_call"] / t["copy_write_factor"]
+
+
+def kernel_probe(args, layers, gemm):
+    """Counter-pass workload: the dominant GEMM call, then a plain device copy of COPY_BYTES."""
+    import torch
+    L = next(L for L in layers if L["name"] == DOMINANT)
+    print(f"probe: nvfp4_gemm W4A4 {DOMINANT} M={L['M']} N={L['N']} K={L['K']} x {args.steps}", flush=True)
+    for _ in range(args.steps):
+        gemm(L)
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    print(f"probe: device copy of {COPY_BYTES} bytes x {args.steps}", flush=True)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("probe: done", flush=True)
+
+
+def time_graph(fns, side, stream, replays=5):
+    """Average duration of one call when the calls in `fns` are captured back to back in one graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for fn in fns:
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * len(fns))
+
+
+def hbm_kernels(side, stream):
+    """Bandwidth-bound calls at sizes well beyond the 256 MB last-level cache: quantize (dynamic and
+    static) and dequantize of a 32768 x 12288 bf16 tensor, and the weight-only GEMM with M = 1 and
+    16 rows cycling through 32 copies of the prepacked weight (~680 MB)."""
+    import torch
+
+    import nvfp4_quantized_gemm_amd as nv
+    import workloads
+
+    dev = "cuda"
+    res = {}
+
+    def entry(us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "bytes": int(nbytes)}
+
+    M, K = 32768, 12288
+    x = workloads.sweep(M, K).to(dev)
+    packed = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    Sst = torch.full((1,), workloads.SWEEP_STATIC_S, dtype=torch.float32, device=dev)
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    n = M * K
+    reps = 10
+    us = time_graph([lambda: nv.nvfp4_quantize(x, S, static=False, packed=packed, scales=scales, workspace=qws)] * reps,
+                    side, stream)
+    res[f"quantize_dynamic_bf16_{M}x{K}"] = entry(us, n * (2 + 2 + 0.5625))
+    us = time_graph([lambda: nv.nvfp4_quantize(x, Sst, static=True, packed=packed, scales=scales)] * reps, side, stream)
+    res[f"quantize_static_bf16_{M}x{K}"] = entry(us, n * (2 + 0.5625))
+    us = time_graph([lambda: nv.nvfp4_dequantize(packed, scales, Sst, torch.bfloat16, out=y)] * reps, side, stream)
+    res[f"dequantize_bf16_{M}x{K}"] = entry(us, n * (0.5625 + 2))
+    del x, packed, scales, y
+    torch.cuda.empty_cache()
+
+    copies = 32
+    for name, (w, acts) in workloads.w4a16(ms=(1, 16)).items():
+        N, Kw = w.shape
+        wp, ws, wS = nv.nvfp4_quantize(w.to(dev))
+        bp = nv.nvfp4_prepack_weight(wp, ws)
+        bps = [bp.clone() for _ in range(copies)]
+        del wp, ws, bp
+        for m, a in acts.items():
+            ad = a.to(dev)
+            out = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            need = nv.nvfp4_gemm_workspace_bytes(nv.W4A16, m, N, Kw)
+            gws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            fns = [(lambda b=b: nv.nvfp4_gemm(nv.W4A16, ad, None, None, b, wS, N, Kw, torch.bfloat16, out=out,
+                                              workspace=gws)) for b in bps]
+            us = time_graph(fns, side, stream)
+            e = entry(us, 0.5625 * N * Kw + 2 * m * Kw + 2 * m * N)
+            e["TFLOPs"] = round(2.0 * m * N * Kw / (us * 1e-6) / 1e12, 2)
+            res[f"w4a16_{name}_M{m}_N{N}_K{Kw}"] = e
+        del bps
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(layers, rows):

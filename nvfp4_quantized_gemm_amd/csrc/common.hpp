@@ -69,4 +69,34 @@ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv &f) {
   return (t + ((n - t) >> 1)) >> (f.shift - 1);
 }
 
+// Lane swaps within quads of lanes (DPP quad_perm): lane i reads lane i ^ 1, or lane i ^ 2.
+__device__ __forceinline__ float swap_lane1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap_lane2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Lane-contiguous element mapping of the bandwidth kernels.  A tensor of M rows x K (K % 16 == 0)
+// is cut into segments of EPL consecutive elements along K, numbered row-major; EPL is chosen so
+// that a segment is 16 bytes of the wide side (8 bf16 or 4 fp32), and consecutive lanes take
+// consecutive segments, so every wave-wide load or store covers one contiguous span.  Segment g
+// lies in 16-value block g / LPB (LPB = 16 / EPL adjacent lanes share a block).
+template <int EPL>
+struct Segments {
+  static constexpr int kLanesPerBlock = 16 / EPL;
+  static constexpr int kShift = (kLanesPerBlock == 2) ? 1 : 2;
+  static_assert(EPL == 8 || EPL == 4, "segments are 8 or 4 elements");
+  // element offset of segment g in a tensor with row stride ld (elements); rows of exactly K
+  // elements (DENSE) need no division, otherwise bpr divides by the blocks per row
+  template <bool DENSE>
+  __device__ static uint64_t offset(uint64_t g, const FastDiv &bpr, int64_t ld) {
+    if (DENSE) return g * EPL;
+    const uint32_t blk = (uint32_t)(g >> kShift);
+    const uint32_t row = fastdiv(blk, bpr);
+    const uint32_t col = (blk - row * bpr.d) * 16u + (uint32_t)(g & (kLanesPerBlock - 1)) * EPL;
+    return (uint64_t)row * (uint64_t)ld + col;
+  }
+};
+
 }  // namespace nvfp4

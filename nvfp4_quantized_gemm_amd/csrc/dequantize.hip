@@ -1,93 +1,100 @@
 // NVFP4 dequantization for gfx950: y = RN32(q * e * S) [NVFP4-DiT page, Definition III.1,
 // Q = s * q with s = e * S].  q * e is exact in fp32 (<= 2 x 4 significant bits), so the single
 // multiply by S is the only rounding; bf16 output rounds that fp32 value to nearest-even
-// (v_cvt_pk_bf16_f32).  One thread owns one 16-value block: 8 B of codes + 1 scale byte in,
-// 64 B (fp32) or 32 B (bf16) out.
+// (v_cvt_pk_bf16_f32).
+//
+// Lane-contiguous: a lane owns one 16-byte segment of the output (8 bf16 or 4 fp32 values), reads
+// its 4 or 2 code bytes and its block's scale byte, so every wave-wide store is one contiguous 1-KB
+// span and the code loads are contiguous too.  Each lane keeps four segments' loads in flight.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
 
-template <int OUT>
-__device__ __forceinline__ void dequant_block(u32x2 w, uint32_t byte, float S, void *y, uint64_t off) {
-  const float e = e4m3_to_f32(byte);
-  const f32x2 q[8] = {fp4_decode2_f32<0>(w.x), fp4_decode2_f32<1>(w.x), fp4_decode2_f32<2>(w.x),
-                      fp4_decode2_f32<3>(w.x), fp4_decode2_f32<0>(w.y), fp4_decode2_f32<1>(w.y),
-                      fp4_decode2_f32<2>(w.y), fp4_decode2_f32<3>(w.y)};
-  float out[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    out[2 * j] = (q[j].x * e) * S;  // q * e is exact; the multiply by S is the one rounding
-    out[2 * j + 1] = (q[j].y * e) * S;
-  }
-  if (OUT == 0) {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x4 o;
-      o.x = __float_as_uint(out[4 * q4]);
-      o.y = __float_as_uint(out[4 * q4 + 1]);
-      o.z = __float_as_uint(out[4 * q4 + 2]);
-      o.w = __float_as_uint(out[4 * q4 + 3]);
-      __builtin_nontemporal_store(o, dst + q4);
-    }
-  } else {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + off);
-#pragma unroll
-    for (int q4 = 0; q4 < 2; ++q4) {
-      uint32_t p[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x2 h = {(__bf16)out[8 * q4 + 2 * t], (__bf16)out[8 * q4 + 2 * t + 1]};
-        p[t] = __builtin_bit_cast(uint32_t, h);
-      }
-      u32x4 o;
-      o.x = p[0];
-      o.y = p[1];
-      o.z = p[2];
-      o.w = p[3];
-      __builtin_nontemporal_store(o, dst + q4);
-    }
-  }
+namespace {
+constexpr int kSegsPerLane = 4;
 }
 
-template <int OUT>
+template <int OUT, bool DENSE>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ packed,
                                                     const uint8_t *__restrict__ scales,
-                                                    const float *__restrict__ tensor_scale, uint32_t nblk,
+                                                    const float *__restrict__ tensor_scale, uint64_t nseg,
                                                     FastDiv bpr, void *__restrict__ y, int64_t ld_y) {
+  constexpr int E = (OUT == 1) ? 8 : 4;  // values per lane segment
+  using Map = Segments<E>;
+  constexpr int U = kSegsPerLane;
   const float S = *tensor_scale;
-  const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t b0 = blockIdx.x * 256u + threadIdx.x; b0 < nblk; b0 += 4 * stride) {
-    u32x2 w[4];
-    uint32_t sb[4];
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
+  for (uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6); t < ntiles; t += gridDim.x * 4ull) {
+    uint32_t codes[U], sb[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // four blocks' loads in flight per thread
-      const uint32_t b = (b0 + u * stride < nblk) ? b0 + u * stride : b0;
-      w[u] = *reinterpret_cast<const u32x2 *>(packed + 8ull * b);
-      sb[u] = scales[b];
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;
+      codes[u] = (E == 8) ? *reinterpret_cast<const uint32_t *>(packed + 4 * g)
+                          : (uint32_t) * reinterpret_cast<const uint16_t *>(packed + 2 * g);
+      sb[u] = scales[g >> Map::kShift];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t b = b0 + u * stride;
-      if (b >= nblk) break;
-      const uint32_t row = fastdiv(b, bpr);
-      const uint32_t col = b - row * bpr.d;
-      dequant_block<OUT>(w[u], sb[u], S, y, (uint64_t)row * (uint64_t)ld_y + 16ull * col);
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = t * (64 * U) + u * 64 + lane;
+      if (g >= nseg) break;
+      const float e = e4m3_to_f32(sb[u]);
+      float out[E];
+      const f32x2 q0 = fp4_decode2_f32<0>(codes[u]), q1 = fp4_decode2_f32<1>(codes[u]);
+      out[0] = (q0.x * e) * S;  // q * e is exact; the multiply by S is the one rounding
+      out[1] = (q0.y * e) * S;
+      out[2] = (q1.x * e) * S;
+      out[3] = (q1.y * e) * S;
+      if (E == 8) {
+        const f32x2 q2 = fp4_decode2_f32<2>(codes[u]), q3 = fp4_decode2_f32<3>(codes[u]);
+        out[4] = (q2.x * e) * S;
+        out[5] = (q2.y * e) * S;
+        out[6] = (q3.x * e) * S;
+        out[7] = (q3.y * e) * S;
+      }
+      const uint64_t off = Map::template offset<DENSE>(g, bpr, ld_y);
+      u32x4 o;
+      if (OUT == 0) {
+        o.x = __float_as_uint(out[0]);
+        o.y = __float_as_uint(out[1]);
+        o.z = __float_as_uint(out[2]);
+        o.w = __float_as_uint(out[3]);
+        *reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off) = o;
+      } else {
+        uint32_t p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 h = {(__bf16)out[2 * j], (__bf16)out[2 * j + 1]};
+          p[j] = __builtin_bit_cast(uint32_t, h);
+        }
+        o.x = p[0];
+        o.y = p[1];
+        o.z = p[2];
+        o.w = p[3];
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + off) = o;
+      }
     }
   }
 }
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
                              int64_t K, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
-  const uint32_t nblk = (uint32_t)(M * (K / 16));
   const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
-  uint32_t g = (nblk + 255u) / 256u;
-  if (g > (uint32_t)kDequantizeMaxGrid) g = kDequantizeMaxGrid;
-  if (out_dtype == 0)
-    k_dequantize<0><<<g, 256, 0, stream>>>(packed, scales, tensor_scale, nblk, bpr, y, ld_y);
-  else
-    k_dequantize<1><<<g, 256, 0, stream>>>(packed, scales, tensor_scale, nblk, bpr, y, ld_y);
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (out_dtype == 0 ? 4u : 8u);
+  const uint64_t tiles = (nseg + 64 * kSegsPerLane - 1) / (64 * kSegsPerLane);
+  uint64_t g = (tiles + 3) / 4;
+  if (g < 1) g = 1;
+  if (g > (uint64_t)kDequantizeMaxGrid) g = kDequantizeMaxGrid;
+  const bool dense = (ld_y == K);
+  if (out_dtype == 0) {
+    if (dense) k_dequantize<0, true><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<0, false><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+  } else {
+    if (dense) k_dequantize<1, true><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<1, false><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+  }
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@
 // sides.  Dequantization in registers: v_cvt_scalef32_pk_{f16,f32}_fp4 with scale 1 gives exact q;
 // one multiply by the block's E4M3 scale gives q * e.  The epilogue multiplies the fp32
 // accumulator by S_A * S_B and converts.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -564,6 +565,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
   }
 }
 
+hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
+                                int64_t ldc, const float *a_ts, const float *b_ts, hipStream_t stream) {
+  int64_t grid = (M * N / 4 + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  if (out_dtype == 0)
+    k_splitk_reduce<0><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts);
+  else
+    k_splitk_reduce<1><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts);
+  return hipGetLastError();
+}
+
 // ---- launchers ----------------------------------------------------------------------------------
 
 template <int MODE, int BM, int BN, int WM, int WN, int OUT>
@@ -610,7 +623,22 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   const int64_t cus = 256;  // planning for the MI355X chip (one workgroup of either tile per CU)
   const int64_t Kc = K / kChunk;
   if (mode == 1) {
+    const int64_t Nu = (N + 31) / 32;
+    if (M <= kSkinnyMaxM) {
+      // streaming: aim for ~4 workgroups per CU, every wave keeping >= 1 chunk
+      pl.variant = GemmVariant::W4A16_Skinny;
+      int64_t sp = (4 * cus + Nu - 1) / Nu;
+      sp = std::min<int64_t>(sp, std::max<int64_t>(1, Kc / 4));
+      if (N % 4 != 0) sp = 1;
+      pl.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 64));
+      return pl;
+    }
     pl.variant = GemmVariant::W4A16_128x256;
+    const int64_t tb = ((M + 127) / 128) * ((N + 255) / 256);
+    int best = 1;
+    for (int sp = 2; sp <= 16; ++sp)
+      if (tb * sp <= cus && Kc / sp >= 6 && N % 4 == 0) best = sp;
+    pl.splits = best;
     return pl;
   }
   const int64_t tmb = (M + 255) / 256, tnb = (N + 255) / 256, tb = tmb * tnb;
@@ -649,10 +677,7 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         float *part = static_cast<float *>(g.workspace);
         hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
         if (e != hipSuccess) return e;
-        int64_t grid = ((int64_t)M * N / 4 + 255) / 256;
-        if (grid > 8192) grid = 8192;
-        k_splitk_reduce<OUT><<<(unsigned)grid, 256, 0, stream>>>(part, pl.splits, M, N, g.c, g.ldc, g.a_ts, g.b_ts);
-        return hipGetLastError();
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, stream);
       }
       if (pl.n_big > 0 && pl.n_big < N) {
         hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, (int)pl.n_big, 1, nullptr, stream);
@@ -663,8 +688,17 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
     }
     case GemmVariant::W4A4_128x128:
       return launch_tiled<0, 128, 128, 2, 2, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
-    case GemmVariant::W4A16_128x256:
+    case GemmVariant::W4A16_128x256: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, stream);
+      }
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
+    case GemmVariant::W4A16_Skinny:
+      return launch_gemm_skinny(g, pl.splits, static_cast<float *>(g.workspace), stream);
     case GemmVariant::Generic:
     default:
       return launch_generic<0, OUT>(g, stream);  // replaced below for W4A16

@@ -19,7 +19,7 @@ hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t 
                           hipStream_t stream);
 hipError_t launch_unpack(const void *in, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales, hipStream_t stream);
 
-enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256 };
+enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256, W4A16_Skinny };
 
 struct GemmPlan {
   GemmVariant variant = GemmVariant::Generic;
@@ -44,5 +44,14 @@ struct GemmArgs {
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
+
+// W4A16 with M <= kSkinnyMaxM: streaming kernel over the prepacked weight (gemm_skinny.hip)
+constexpr int kSkinnyMaxM = 32;
+hipError_t launch_gemm_skinny(const GemmArgs &g, int splits, float *partial, hipStream_t stream);
+
+// C = (sum of the splits' fp32 partials [splits][M][N], in order) * (a_ts ? *a_ts : 1) * *b_ts;
+// needs N % 4 == 0
+hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
+                                int64_t ldc, const float *a_ts, const float *b_ts, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -6,10 +6,14 @@
 // saturating at +-6), sign bit copied from v, two codes per byte, low nibble first.  Decisions are
 // taken on the exact real quotients.
 //
-// Data flow: one thread owns one 16-value block (32 B of bf16 or 64 B of fp32 in, 8 B of codes
-// and 1 scale byte out), so a wave streams 2-4 KB of contiguous input and writes 512 B + 64 B.
-// Dynamic mode runs k_amax first (per-workgroup partial maxima, no atomics, deterministic); every
-// quantize workgroup reduces those partials itself and derives S = RN32(amax / 2688).
+// Data flow: lane-contiguous.  A lane owns one 16-byte segment of the input (8 bf16 or 4 fp32
+// values), so each wave-wide load is one contiguous 1-KB span; the 2 (bf16) or 4 (fp32) lanes of a
+// 16-value block combine their maxima with cross-lane swaps, every lane derives the block's scale
+// byte and encodes its own values, lanes store their 4 (bf16) or 2 (fp32) code bytes contiguously
+// and the first lane of each block stores the scale byte.  Each lane keeps four segments' loads in
+// flight.  Dynamic mode runs k_amax first (same mapping, per-workgroup partial maxima, no atomics,
+// deterministic); every quantize workgroup reduces those partials itself and derives
+// S = RN32(amax / 2688).
 //
 // Exactness (all fast paths bracket the exact real quotient and fall back when unsure):
 //  * Block scale.  With c = 1/(6 S) (fp64, once per workgroup), rl = RN32(amax RN32(c (1 - 2^-20)))
@@ -32,42 +36,42 @@
 
 namespace nvfp4 {
 
-// ---- input loading ------------------------------------------------------------------------------
+// ---- input loading: one 16-byte segment per lane ------------------------------------------------
 
 template <int DT>
-struct BlockIn;
+struct SegIn;
 
 template <>
-struct BlockIn<0> {  // fp32
-  __device__ static void load(const void *base, uint64_t elem_off, float v[16]) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem_off);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 w = p[q];
-      v[4 * q + 0] = __uint_as_float(w.x);
-      v[4 * q + 1] = __uint_as_float(w.y);
-      v[4 * q + 2] = __uint_as_float(w.z);
-      v[4 * q + 3] = __uint_as_float(w.w);
-    }
+struct SegIn<0> {  // fp32: 4 values
+  static constexpr int kElems = 4;
+  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
+    return *reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem_off);
+  }
+  __device__ static void unpack(const u32x4 &w, float v[4]) {
+    v[0] = __uint_as_float(w.x);
+    v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z);
+    v[3] = __uint_as_float(w.w);
   }
 };
 
 template <>
-struct BlockIn<1> {  // bf16
-  __device__ static void load(const void *base, uint64_t elem_off, float v[16]) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem_off);
+struct SegIn<1> {  // bf16: 8 values
+  static constexpr int kElems = 8;
+  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
+    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem_off);
+  }
+  __device__ static void unpack(const u32x4 &w, float v[8]) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      u32x4 w = p[q];
-      uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[8 * q + 2 * t] = bf16lo(a[t]);
-        v[8 * q + 2 * t + 1] = bf16hi(a[t]);
-      }
+    for (int t = 0; t < 4; ++t) {
+      v[2 * t] = bf16lo(a[t]);
+      v[2 * t + 1] = bf16hi(a[t]);
     }
   }
 };
+
+constexpr int kSegsPerLane = 4;  // segments in flight per lane
 
 // ---- exact pieces ---------------------------------------------------------------------------------
 
@@ -103,7 +107,9 @@ __device__ __forceinline__ float ru32(double d) {
 // Exact code magnitudes through per-block thresholds.  Boundaries between consecutive E2M1 grid
 // values at t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}; a tie rounds to the even code, i.e. down at
 // 0.25, 1.25, 2.5, 5 and up at 0.75, 1.75, 3.5.  U_k is the least fp32 value whose code is >= k.
-__device__ __forceinline__ void codes_exact(const float v[16], float e, float S, uint32_t &w0, uint32_t &w1) {
+// Returns the n codes of v (n <= 8), value i in nibble i.
+template <int N>
+__device__ __forceinline__ uint32_t codes_exact(const float *v, float e, float S) {
   const double es = (double)e * (double)S;  // exact: 4 x 24 significant bits
   float U[7];
   U[0] = next_up(rd32(0.25 * es));
@@ -113,57 +119,112 @@ __device__ __forceinline__ void codes_exact(const float v[16], float e, float S,
   U[4] = next_up(rd32(2.5 * es));
   U[5] = ru32(3.5 * es);
   U[6] = next_up(rd32(5.0 * es));
-  uint32_t out[2] = {0u, 0u};
+  uint32_t out = 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float a = fabsf(v[i]);
+  for (int i = 0; i < N; ++i) {
+    const float a = fabsf(v[i]);
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < 7; ++k) m += (a >= U[k]) ? 1u : 0u;
     m |= (__float_as_uint(v[i]) >> 28) & 8u;
-    out[i >> 3] |= m << (4 * (i & 7));
+    out |= m << (4 * i);
   }
-  w0 = out[0];
-  w1 = out[1];
+  return out;
+}
+
+// Codes of the n = 4 or 8 values of one lane under block scale byte `byte` (nonzero) and tensor
+// scale S: bracketing fast path, exact thresholds when the bracket is ambiguous or S is extreme.
+//
+// ties_only: S is a power of two and the input is bf16.  Then every value and every boundary
+// t e S has at most 8 significant bits at the same scale, so a value that is not exactly on a
+// boundary differs from it by at least 2^-8 relative, far outside the 2^-19 bracket: an
+// ambiguous bracket is an exact tie, whose code is the even one of the two adjacent bracketing
+// codes (ties to even).  That choice is made for all nibbles at once with integer operations.
+template <int N>
+__device__ __forceinline__ uint32_t encode_values(const float *v, uint32_t byte, float S, float invS, bool fast_ok,
+                                                  bool ties_only) {
+  const float e = e4m3_to_f32(byte);
+  if (fast_ok) {
+    const float inv = __builtin_amdgcn_rcpf(e) * invS;
+    const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
+    uint32_t lo = 0, hi = 0;
+    lo = fp4_encode2<0>(lo, v[0] * ilo, v[1] * ilo);
+    hi = fp4_encode2<0>(hi, v[0] * ihi, v[1] * ihi);
+    lo = fp4_encode2<1>(lo, v[2] * ilo, v[3] * ilo);
+    hi = fp4_encode2<1>(hi, v[2] * ihi, v[3] * ihi);
+    if (N == 8) {
+      lo = fp4_encode2<2>(lo, v[4] * ilo, v[5] * ilo);
+      hi = fp4_encode2<2>(hi, v[4] * ihi, v[5] * ihi);
+      lo = fp4_encode2<3>(lo, v[6] * ilo, v[7] * ilo);
+      hi = fp4_encode2<3>(hi, v[6] * ihi, v[7] * ihi);
+    }
+    if (lo == hi) return lo;
+    if (ties_only) {
+      const uint32_t amb = lo ^ hi;
+      uint32_t d = amb | (amb >> 1);
+      d |= d >> 2;                                   // bit 4i set iff nibble i differs
+      const uint32_t pick = d & lo & 0x11111111u;     // differing nibbles whose lower code is odd
+      const uint32_t m = pick * 15u;                  // widen to whole nibbles (no carries)
+      return (lo & ~m) | (hi & m);
+    }
+  }
+  return codes_exact<N>(v, e, S);
+}
+
+// E4M3 byte of the block maximum amax (>= 0) under S: bracketing fast path, exact fallback.
+__device__ __forceinline__ uint32_t block_byte(float amax, float S, float rlo, float rhi, bool fast_ok) {
+  if (!(amax > 0.0f)) return 0u;
+  if (fast_ok) {
+    const float ra = fminf(amax * rlo, kE4M3Max), rb = fminf(amax * rhi, kE4M3Max);
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
+    if ((pk & 0xffu) == ((pk >> 8) & 0xffu)) return pk & 0xffu;
+  }
+  return scale_byte_exact(amax, S);
 }
 
 // ---- dynamic amax: per-workgroup partial maxima ------------------------------------------------------
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_t ld, uint32_t nblk,
+template <int DT, bool DENSE>
+__global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                               FastDiv bpr, float *__restrict__ partial) {
+  using In = SegIn<DT>;
+  using Map = Segments<In::kElems>;
+  constexpr int U = kSegsPerLane;
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
   float m = 0.0f;
-  const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t b0 = blockIdx.x * 256u + threadIdx.x; b0 < nblk; b0 += 4 * stride) {
-    float v[4][16];
+  for (uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6); t < ntiles; t += gridDim.x * 4ull) {
+    float v[U][In::kElems];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // four blocks' loads in flight per thread
-      const uint32_t b = (b0 + u * stride < nblk) ? b0 + u * stride : b0;
-      const uint32_t row = fastdiv(b, bpr);
-      const uint32_t col = b - row * bpr.d;
-      BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v[u]);
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;  // a repeated segment does not change the maximum
+      In::unpack(In::raw(x, Map::template offset<DENSE>(g, bpr, ld)), v[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[u][i]));
+      for (int i = 0; i < In::kElems; ++i) m = fmaxf(m, fabsf(v[u][i]));
   }
-  // workgroup reduction
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if (lane == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---- quantize ------------------------------------------------------------------------------------
 
-template <int DT, bool DYNAMIC>
-__global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint32_t nblk,
+template <int DT, bool DYNAMIC, bool DENSE>
+__global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                                   FastDiv bpr, uint8_t *__restrict__ packed,
                                                   uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
                                                   const float *__restrict__ partial, int npartial) {
+  using In = SegIn<DT>;
+  constexpr int E = In::kElems;
+  using Map = Segments<E>;
+  constexpr int U = kSegsPerLane;
   __shared__ float s_S;
   if (DYNAMIC) {
     float m = 0.0f;
@@ -174,8 +235,8 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-      float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      float S = amax / kDynDivisor;  // correctly rounded fp32 division
+      const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const float S = amax / kDynDivisor;  // correctly rounded fp32 division
       s_S = S;
       if (blockIdx.x == 0) *tensor_scale = S;
     }
@@ -189,106 +250,91 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   const double c6 = fast_ok ? 1.0 / (6.0 * (double)S) : 0.0;
   const float rlo = (float)(c6 * (1.0 - 0x1p-20)), rhi = (float)(c6 * (1.0 + 0x1p-20));
   const float invS = fast_ok ? (float)(1.0 / (double)S) : 0.0f;
+  const bool ties_only = (DT == 1) && fast_ok && ((__float_as_uint(S) & 0x007fffffu) == 0u);
 
-  const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t b0 = blockIdx.x * 256u + threadIdx.x; b0 < nblk; b0 += 2 * stride) {
-    // two blocks per thread per iteration: both loads are in flight before any compute
-    const uint32_t bb[2] = {b0, b0 + stride};
-    float v[2][16];
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
+  const uint64_t tstride = gridDim.x * 4ull;
+  auto fetch = [&](uint64_t t, u32x4 *r) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t b = bb[u] < nblk ? bb[u] : b0;
-      const uint32_t row = fastdiv(b, bpr);
-      const uint32_t col = b - row * bpr.d;
-      BlockIn<DT>::load(x, (uint64_t)row * (uint64_t)ld + 16u * col, v[u]);
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;
+      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
     }
+  };
+  uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
+  u32x4 nxt[U];
+  if (t < ntiles) fetch(t, nxt);
+  for (; t < ntiles; t += tstride) {
+    // the next tile's loads are issued before this tile is encoded
+    u32x4 cur[U];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t b = bb[u];
-      if (b >= nblk) break;
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    if (t + tstride < ntiles) fetch(t + tstride, nxt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = t * (64 * U) + u * 64 + lane;
+      float v[E];
+      In::unpack(cur[u], v);
+      // block maximum over the block's lanes (nseg is a multiple of the lanes per block, so a
+      // block's lanes are all in range or all out of range)
       float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
-
-      uint32_t byte = 0, w0 = 0, w1 = 0;
-      if (amax > 0.0f) {
-        if (fast_ok) {
-          const float ra = fminf(amax * rlo, kE4M3Max), rb = fminf(amax * rhi, kE4M3Max);
-          const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
-          byte = pk & 0xffu;
-          if (byte != ((pk >> 8) & 0xffu)) byte = scale_byte_exact(amax, S);
-        } else {
-          byte = scale_byte_exact(amax, S);
-        }
-      }
-      if (byte == 0) {
-        // zero or flushed block: magnitude 0, sign copied
+      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      amax = fmaxf(amax, swap_lane1(amax));
+      if (Map::kLanesPerBlock == 4) amax = fmaxf(amax, swap_lane2(amax));
+      if (g >= nseg) continue;
+      const uint32_t byte = block_byte(amax, S, rlo, rhi, fast_ok);
+      uint32_t codes;
+      if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
+        codes = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t sgn = (__float_as_uint(v[u][i]) >> 28) & 8u;
-          if (i < 8) w0 |= sgn << (4 * i);
-          else w1 |= sgn << (4 * (i - 8));
-        }
+        for (int i = 0; i < E; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
       } else {
-        const float e = e4m3_to_f32(byte);
-        bool exact = !fast_ok;
-        if (fast_ok) {
-          const float inv = __builtin_amdgcn_rcpf(e) * invS;
-          const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
-          uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
-#define NVFP4_ENC(J)                                                              \
-  l0 = fp4_encode2<J>(l0, v[u][2 * J] * ilo, v[u][2 * J + 1] * ilo);             \
-  h0 = fp4_encode2<J>(h0, v[u][2 * J] * ihi, v[u][2 * J + 1] * ihi);             \
-  l1 = fp4_encode2<J>(l1, v[u][8 + 2 * J] * ilo, v[u][9 + 2 * J] * ilo);         \
-  h1 = fp4_encode2<J>(h1, v[u][8 + 2 * J] * ihi, v[u][9 + 2 * J] * ihi);
-          NVFP4_ENC(0)
-          NVFP4_ENC(1)
-          NVFP4_ENC(2)
-          NVFP4_ENC(3)
-#undef NVFP4_ENC
-          w0 = l0;
-          w1 = l1;
-          exact = (l0 != h0) || (l1 != h1);
-        }
-        if (exact) codes_exact(v[u], e, S, w0, w1);
+        codes = encode_values<E>(v, byte, S, invS, fast_ok, ties_only);
       }
-      u32x2 o;
-      o.x = w0;
-      o.y = w1;
-      *reinterpret_cast<u32x2 *>(packed + 8ull * b) = o;
-      scales[b] = (uint8_t)byte;
+      if (E == 8) *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
+      else *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
+      if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)byte;
     }
   }
 }
 
 // ---- launchers -------------------------------------------------------------------------------------
 
-static int grid_for(uint32_t nblk, int cap) {
-  uint32_t g = (nblk + 255u) / 256u;
+static int grid_for(uint64_t nseg, int cap) {
+  const uint64_t tiles = (nseg + 64 * kSegsPerLane - 1) / (64 * kSegsPerLane);
+  uint64_t g = (tiles + 3) / 4;  // four waves per workgroup
   if (g < 1) g = 1;
-  return (int)(g > (uint32_t)cap ? (uint32_t)cap : g);
+  return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
+}
+
+template <int DT, bool DENSE>
+static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr, uint8_t *packed, uint8_t *scales,
+                         float *tensor_scale, bool dynamic, float *partial, hipStream_t stream) {
+  const int gq = grid_for(nseg, kQuantizeMaxGrid);
+  if (dynamic) {
+    const int ga = grid_for(nseg, kAmaxPartials);
+    k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr, partial);
+    k_quantize<DT, true, DENSE><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, partial, ga);
+  } else {
+    k_quantize<DT, false, DENSE><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, nullptr, 0);
+  }
 }
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
                            uint8_t *scales, float *tensor_scale, bool dynamic, float *partial,
                            hipStream_t stream) {
-  const uint32_t bpr_n = (uint32_t)(K / 16);
-  const uint32_t nblk = (uint32_t)(M * (K / 16));
-  const FastDiv bpr = make_fastdiv(bpr_n);
-  const int gq = grid_for(nblk, kQuantizeMaxGrid);
-  if (dynamic) {
-    const int ga = grid_for(nblk, kAmaxPartials);
-    if (dtype == 0) k_amax<0><<<ga, 256, 0, stream>>>(x, ld, nblk, bpr, partial);
-    else k_amax<1><<<ga, 256, 0, stream>>>(x, ld, nblk, bpr, partial);
-    if (dtype == 0)
-      k_quantize<0, true><<<gq, 256, 0, stream>>>(x, ld, nblk, bpr, packed, scales, tensor_scale, partial, ga);
-    else
-      k_quantize<1, true><<<gq, 256, 0, stream>>>(x, ld, nblk, bpr, packed, scales, tensor_scale, partial, ga);
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
+  const bool dense = (ld == K);
+  if (dtype == 0) {
+    if (dense) run_quantize<0, true>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
+    else run_quantize<0, false>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
   } else {
-    if (dtype == 0)
-      k_quantize<0, false><<<gq, 256, 0, stream>>>(x, ld, nblk, bpr, packed, scales, tensor_scale, nullptr, 0);
-    else
-      k_quantize<1, false><<<gq, 256, 0, stream>>>(x, ld, nblk, bpr, packed, scales, tensor_scale, nullptr, 0);
+    if (dense) run_quantize<1, true>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
+    else run_quantize<1, false>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
   }
   return hipGetLastError();
 }

@@ -321,7 +321,11 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
     check_gemm(Yg[:, cols], Y, R, out_dtype == torch.bfloat16, f"W4A16 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 96, 256), (37, 200, 1152), (300, 130, 384), (5, 48, 80)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 96, 256), (37, 200, 1152), (300, 130, 384), (5, 48, 80),
+                                   # streaming kernel (M <= 32): K split over workgroups, ragged last unit
+                                   (1, 1000, 2048), (31, 1000, 2048), (7, 98, 1536), (16, 4096, 3072),
+                                   # tiled kernel with K split
+                                   (200, 520, 2048)])
 def test_gemm_w4a16_ragged(M, N, K):
     g = torch.Generator().manual_seed(M * 5 + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
