@@ -625,12 +625,14 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   if (mode == 1) {
     const int64_t Nu = (N + 31) / 32;
     if (M <= kSkinnyMaxM) {
-      // streaming: aim for ~4 workgroups per CU, every wave keeping >= 1 chunk
+      // streaming: >= ~1.5 workgroups per CU; narrow N splits K across workgroups (each split
+      // keeps >= 16 chunks); waves per workgroup grow with the chunks per split
       pl.variant = GemmVariant::W4A16_Skinny;
-      int64_t sp = (4 * cus + Nu - 1) / Nu;
-      sp = std::min<int64_t>(sp, std::max<int64_t>(1, Kc / 4));
-      if (N % 4 != 0) sp = 1;
-      pl.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 64));
+      int64_t sp = 1;
+      while (Nu * sp < (3 * cus) / 2 && Kc / (2 * sp) >= 16 && N % 4 == 0) sp *= 2;
+      pl.splits = (int)sp;
+      const int64_t per = Kc / sp;
+      pl.waves = per >= 48 ? 16 : (per >= 16 ? 8 : 4);
       return pl;
     }
     pl.variant = GemmVariant::W4A16_128x256;
@@ -664,7 +666,7 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
 }
 
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
-  const GemmPlan pl = plan_gemm(mode, M, N, K, mode == 0 ? K : K);
+  const GemmPlan pl = plan_gemm(mode, M, N, K, K);
   return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -698,7 +700,7 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A16_Skinny:
-      return launch_gemm_skinny(g, pl.splits, static_cast<float *>(g.workspace), stream);
+      return launch_gemm_skinny(g, pl.waves, pl.splits, static_cast<float *>(g.workspace), stream);
     case GemmVariant::Generic:
     default:
       return launch_generic<0, OUT>(g, stream);  // replaced below for W4A16

@@ -24,6 +24,7 @@ enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256, W4A
 struct GemmPlan {
   GemmVariant variant = GemmVariant::Generic;
   int splits = 1;     // K splits (partial tiles reduced by a second kernel)
+  int waves = 4;      // W4A16_Skinny: waves per workgroup
   int64_t n_big = 0;  // > 0: columns [0, n_big) in 256x256 tiles, the rest in 128x128 tiles
 };
 
@@ -47,7 +48,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 
 // W4A16 with M <= kSkinnyMaxM: streaming kernel over the prepacked weight (gemm_skinny.hip)
 constexpr int kSkinnyMaxM = 32;
-hipError_t launch_gemm_skinny(const GemmArgs &g, int splits, float *partial, hipStream_t stream);
+hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *partial, hipStream_t stream);
 
 // C = (sum of the splits' fp32 partials [splits][M][N], in order) * (a_ts ? *a_ts : 1) * *b_ts;
 // needs N % 4 == 0

@@ -323,7 +323,7 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 96, 256), (37, 200, 1152), (300, 130, 384), (5, 48, 80),
                                    # streaming kernel (M <= 32): K split over workgroups, ragged last unit
-                                   (1, 1000, 2048), (31, 1000, 2048), (7, 98, 1536), (16, 4096, 3072),
+                                   (1, 1000, 2048), (31, 1000, 2048), (7, 98, 1536), (16, 4096, 3072), (3, 200, 4096),
                                    # tiled kernel with K split
                                    (200, 520, 2048)])
 def test_gemm_w4a16_ragged(M, N, K):
