@@ -225,6 +225,22 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   constexpr int E = In::kElems;
   using Map = Segments<E>;
   constexpr int U = kSegsPerLane;
+  // the first tile's input loads are independent of S: issue them before the scale reduction
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
+  const uint64_t tstride = gridDim.x * 4ull;
+  auto fetch = [&](uint64_t t, u32x4 *r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;
+      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
+    }
+  };
+  uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
+  u32x4 nxt[U];
+  if (t < ntiles) fetch(t, nxt);
+
   __shared__ float s_S;
   if (DYNAMIC) {
     float m = 0.0f;
@@ -252,20 +268,6 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   const float invS = fast_ok ? (float)(1.0 / (double)S) : 0.0f;
   const bool ties_only = (DT == 1) && fast_ok && ((__float_as_uint(S) & 0x007fffffu) == 0u);
 
-  const int lane = threadIdx.x & 63;
-  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
-  const uint64_t tstride = gridDim.x * 4ull;
-  auto fetch = [&](uint64_t t, u32x4 *r) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint64_t g = t * (64 * U) + u * 64 + lane;
-      g = g < nseg ? g : nseg - 1;
-      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
-    }
-  };
-  uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
-  u32x4 nxt[U];
-  if (t < ntiles) fetch(t, nxt);
   for (; t < ntiles; t += tstride) {
     // the next tile's loads are issued before this tile is encoded
     u32x4 cur[U];
