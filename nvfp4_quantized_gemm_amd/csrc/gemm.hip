@@ -90,7 +90,8 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // columns 8 g + 4 (l / 32) + 0..3.  Each 32-row slab of a wave's sub-tile is written to a
 // wave-private, padded, row-major LDS region (one 8- or 16-byte write per column group) and read
 // back row-contiguously, so every global store instruction covers whole rows of the sub-tile with
-// 16-byte lane stores.
+// 16-byte lane stores.  `vec` says the rows of C are 16-byte aligned; a lane whose 16 bytes lie
+// inside C stores them at once, lanes at the ragged edge store element by element.
 template <int CW, int ES>
 struct EpiPitch {
   static constexpr int kPitch = CW * ES + 16;  // row pitch in bytes (16-B pad against bank conflicts)
@@ -140,13 +141,19 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
       const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r * kPitch + cq * ES);
       const int row = row0 + i * 32 + r, col = col0 + cq;
       OutT *pc = C + (int64_t)row * ldc + col;
-      if (vec) {
+      if (vec && row < M && col + kEl <= N) {
         *reinterpret_cast<u32x4 *>(pc) = v;
-      } else if (row < M) {
-        const OutT *e = reinterpret_cast<const OutT *>(&v);
+      } else if (row < M && col < N) {
+        // ragged edge: element by element (elements taken out of the registers by shifts, so the
+        // staged vector never goes through memory)
 #pragma unroll
-        for (int q = 0; q < kEl; ++q)
-          if (col + q < N) pc[q] = e[q];
+        for (int q = 0; q < kEl; ++q) {
+          if (col + q < N) {
+            const uint32_t word = v[(q * ES) / 4];
+            if (ES == 4) reinterpret_cast<uint32_t *>(pc)[q] = word;
+            else reinterpret_cast<uint16_t *>(pc)[q] = (uint16_t)(word >> (16 * (q & 1)));
+          }
+        }
       }
     }
     wave_lds_sync();  // the next slab overwrites this region
@@ -463,19 +470,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- epilogue: scale by S_A * S_B, convert, store ---------------------------------------------
-  __syncthreads();  // every wave is done reading the LDS ring; it now stages output
+  wait_vmem();      // the loop's last look-ahead DMA targets the ring, which now stages output
+  __syncthreads();  // every wave is done reading the LDS ring
   uint8_t *lds_wave = smem + wave * (32 * EpiPitch<BN / WN, 4>::kPitch);
   const int row0 = m0 + wm * (BM / WM), col0 = n0 + wn * (BN / WN);
   if (splits > 1) {
     // unscaled fp32 partial tile -> partial[split][M][N]; the reduce kernel scales and converts
-    const bool vec = (m0 + BM <= M) && (n0 + BN <= N) && (N % 4 == 0);
+    const bool vec = (N % 4 == 0);  // 16-byte aligned rows; lanes check their own bounds
     store_tile<BN / WN, TM, TN, float>(acc, 1.0f, partial + (int64_t)split * M * N, N, M, N, row0, col0, vec,
                                        lds_wave, lane);
     return;
   }
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
   typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
-  const bool vec = (m0 + BM <= M) && (n0 + BN <= N) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+  const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;  // 16-byte aligned rows
   store_tile<BN / WN, TM, TN, OutT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec, lds_wave, lane);
 }
 
