@@ -84,6 +84,15 @@ __device__ __forceinline__ void g2l4(const void *g, uint8_t *lds) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are outstanding (they complete in
+// issue order), then meet the other waves at a bare barrier: unlike __syncthreads() this does not
+// also wait for the loads issued after the ones needed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Output staging.  The MFMAs compute C^T tiles (the B fragment is the row operand), so lane l of
 // 32x32 tile (i, j) holds output row r = l % 32 of the tile and, for g = 0..3, the four consecutive
@@ -352,20 +361,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
+    // Prologue: start on chunk 0 as soon as it has landed; chunk 1 keeps streaming and is waited
+    // for in the first chunk's step 3, right before its first LDS read.
+    constexpr int kPer = (NSLOT + 5) / 6;                                 // DMA loads per step
+    constexpr int kIssuedBefore3 = (3 * kPer < NSLOT) ? 3 * kPer : NSLOT;  // issued in steps 0-2
     const int nk = kend - kbeg;
     issue(kbeg, 0);
-    if (nk > 1) issue(kbeg + 1, 1);
-    wait_vmem();
-    __syncthreads();
+    if (nk > 1) {
+      issue(kbeg + 1, 1);
+      wait_vmem_then_barrier<NSLOT>();  // this wave's chunk-0 loads (chunk 1's may be in flight)
+    } else {
+      wait_vmem_then_barrier<0>();
+    }
     read_part(P0a, P0b, 0, 0);
     read_scales(0);
     cvt_scales(Ea, Eb);
     deq(P0a, P0b, Ea, Eb, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int kc = 0; kc < nk; ++kc) {
+    // One chunk of 8 steps.  FIRST (compile time) is the peeled first chunk: it has no top wait
+    // but waits for chunk 1 before step 3; later chunks wait for the next chunk at the top.
+    auto chunk = [&](int kc, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
       const int cur = kc % 3;
-      if (kc > 0) {
+      if (!FIRST) {
         wait_vmem();  // this wave's DMA of chunk kc+1 (issued one chunk ago) has landed
         __syncthreads();
       }
@@ -379,8 +398,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int slot = s & 1;
+        if (FIRST && s == 3) {
+          // chunk 1 (issued in the prologue, before this chunk's DMA) must have landed everywhere
+          if (nk > 1) wait_vmem_then_barrier<kIssuedBefore3>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // spread chunk kc+2's DMA over the steps: a VMEM issue stall then overlaps running MFMAs
-        constexpr int kPer = (NSLOT + 5) / 6;
 #pragma unroll
         for (int u = 0; u < kPer; ++u)
           if (s * kPer + u < NSLOT) issue_slot(kdma, bdma, s * kPer + u);
@@ -401,7 +424,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int i = 0; i < TM; ++i) { Ea[i][0] = Na[i][0]; Ea[i][1] = Na[i][1]; }
 #pragma unroll
       for (int j = 0; j < TN; ++j) { Eb[j][0] = Nb[j][0]; Eb[j][1] = Nb[j][1]; }
-    }
+    };
+    chunk(0, std::true_type{});
+    for (int kc = 1; kc < nk; ++kc) chunk(kc, std::false_type{});
   } else {
     // ---- W4A16: chunk fragments into registers, next chunk's DMA, 8 pipelined steps ----
     const int nk = kend - kbeg;
