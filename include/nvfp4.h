@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
-  NVFP4_ERR_SHAPE = 2,     /* M < 1, N < 1, K < 16, K % 16 != 0, or a size overflow */
+  NVFP4_ERR_SHAPE = 2,     /* M < 0, N < 0, K < 16, K % 16 != 0, or a size overflow */
   NVFP4_ERR_STRIDE = 3,    /* a leading dimension is smaller than the row it must hold */
   NVFP4_ERR_ALIGN = 4,     /* a pointer or row pitch breaks the stated alignment */
   NVFP4_ERR_DTYPE = 5,     /* unknown dtype, or a dtype the call does not accept */
@@ -79,7 +79,9 @@ int nvfp4_abi_version(void);
  *
  *   x            device, [M][ld_x] elements of x_dtype (fp32 or bf16), 16-byte aligned,
  *                ld_x * sizeof(elem) a multiple of 16.  Only the first K of each row are read.
- *   M, K         M >= 1; K >= 16 and K % 16 == 0.
+ *   M, K         M >= 0; K >= 16 and K % 16 == 0.  M == 0 (an empty tensor) is valid: nothing
+ *                is read or written, except that DYNAMIC writes S = 0 (the maximum over no
+ *                element is taken as 0); x, packed and scales may then be NULL.
  *   packed       device, [M][K/2] bytes, written.  8-byte aligned.
  *   scales       device, [M][K/16] E4M3 bytes, written.
  *   tensor_scale device, one fp32: written by DYNAMIC, read by STATIC (finite, > 0).
@@ -103,6 +105,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, i
  *                                 (packed 8-byte aligned).
  *   y            device, [M][ld_y] of y_dtype, 16-byte aligned, ld_y * sizeof(elem) % 16 == 0,
  *                ld_y >= K.  Columns K..ld_y-1 are not written.
+ *   M == 0 is valid and touches nothing (every pointer may then be NULL).
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
                                 int64_t M, int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
@@ -114,7 +117,8 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, co
  * to a multiple of 32 and K to a multiple of 128 with zero codes and zero scales.  The layout is
  * opaque; its size is nvfp4_prepacked_bytes(N, K).  prepacked must be 16-byte aligned.  The
  * weight's tensor scale is not part of it and is passed to nvfp4_gemm separately.
- * nvfp4_unpack_weight is the exact inverse (for inspection and tests).
+ * nvfp4_unpack_weight is the exact inverse (for inspection and tests).  N == 0 is valid and
+ * touches nothing (nvfp4_prepacked_bytes(0, K) == 0).
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_prepacked_bytes(int64_t N, int64_t K);
 nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
@@ -138,6 +142,7 @@ nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, 
  *   c              device, [M][ldc] of c_dtype (fp32 or bf16), ldc >= N, base 16-byte aligned.
  *   workspace      device scratch of nvfp4_gemm_workspace_bytes(mode, M, N, K) bytes (may be NULL
  *                  when that is 0), 16-byte aligned; contents need no initialization.
+ *   M == 0 or N == 0 (an empty output) is valid and touches nothing; the pointers may be NULL.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
 nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,

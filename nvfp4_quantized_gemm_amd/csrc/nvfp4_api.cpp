@@ -16,8 +16,9 @@ constexpr int64_t kMaxElems = (int64_t)1 << 40;  // guards 64-bit size arithmeti
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// M == 0 (an empty tensor) is valid; K must name whole 16-value blocks.
 nvfp4_status_t check_mk(int64_t M, int64_t K) {
-  if (M < 1 || K < 16 || (K % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (M < 0 || K < 16 || (K % 16) != 0) return NVFP4_ERR_SHAPE;
   if (M > kMaxElems / K) return NVFP4_ERR_SHAPE;
   if (M * (K / 16) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;  // 32-bit block index
   return NVFP4_OK;
@@ -73,11 +74,13 @@ size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K) {
 nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                               uint8_t *packed, uint8_t *scales, float *tensor_scale, nvfp4_scale_mode_t mode,
                               void *workspace, size_t workspace_bytes, void *stream) {
-  if (!x || !packed || !scales || !tensor_scale) return NVFP4_ERR_NULL;
+  if (!tensor_scale) return NVFP4_ERR_NULL;
   if (!valid_dtype(x_dtype)) return NVFP4_ERR_DTYPE;
   if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
   nvfp4_status_t st = check_mk(M, K);
   if (st != NVFP4_OK) return st;
+  if (M > 0 && (!x || !packed || !scales)) return NVFP4_ERR_NULL;
+  if (M == 0 && mode == NVFP4_SCALE_STATIC) return NVFP4_OK;  // nothing to read or write
   if (ld_x < K) return NVFP4_ERR_STRIDE;
   const int es = elem_size(x_dtype);
   if (!aligned(x, 16) || ((ld_x * es) % 16) != 0 || !aligned(packed, 8) || !aligned(tensor_scale, 4))
@@ -95,10 +98,11 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, i
 
 nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
                                 int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
-  if (!packed || !scales || !tensor_scale || !y) return NVFP4_ERR_NULL;
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
   nvfp4_status_t st = check_mk(M, K);
   if (st != NVFP4_OK) return st;
+  if (M == 0) return NVFP4_OK;  // empty: nothing to read or write
+  if (!packed || !scales || !tensor_scale || !y) return NVFP4_ERR_NULL;
   if (ld_y < K) return NVFP4_ERR_STRIDE;
   const int es = elem_size(y_dtype);
   if (!aligned(y, 16) || ((ld_y * es) % 16) != 0 || !aligned(packed, 8) || !aligned(tensor_scale, 4))
@@ -110,16 +114,17 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, co
 }
 
 size_t nvfp4_prepacked_bytes(int64_t N, int64_t K) {
-  if (N < 1 || K < 16 || (K % 16) != 0 || N > kMaxElems / K) return 0;
+  if (N < 0 || K < 16 || (K % 16) != 0 || N > kMaxElems / K) return 0;
   const int64_t Nu = (N + 31) / 32, Kc = (K + 127) / 128;
   return (size_t)(Nu * Kc * (2048 + 256));
 }
 
 nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
                                     void *prepacked, void *stream) {
-  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   nvfp4_status_t st = check_mk(N, K);
   if (st != NVFP4_OK) return st;
+  if (N == 0) return NVFP4_OK;  // empty weight
+  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
@@ -128,9 +133,10 @@ nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales
 
 nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
                                    void *stream) {
-  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   nvfp4_status_t st = check_mk(N, K);
   if (st != NVFP4_OK) return st;
+  if (N == 0) return NVFP4_OK;  // empty weight
+  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
@@ -139,7 +145,7 @@ nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, 
 
 size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return 0;
-  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0) return 0;
+  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0) return 0;  // empty calls need no workspace
   return gemm_workspace_bytes((int)mode, M, N, K);
 }
 
@@ -148,13 +154,14 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
                           int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
                           size_t workspace_bytes, void *stream) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return NVFP4_ERR_MODE;
-  if (!a || !b_prepacked || !b_tensor_scale || !c) return NVFP4_ERR_NULL;
-  if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
   if (mode == NVFP4_W4A16 && (a_scales || a_tensor_scale)) return NVFP4_ERR_NULL;
   if (!valid_dtype(c_dtype)) return NVFP4_ERR_DTYPE;
-  if (N < 1) return NVFP4_ERR_SHAPE;
+  if (N < 0) return NVFP4_ERR_SHAPE;
   nvfp4_status_t st = check_mk(M, K);
   if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;  // empty output: nothing to read or write
+  if (!a || !b_prepacked || !b_tensor_scale || !c) return NVFP4_ERR_NULL;
+  if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
   if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
   if (lda < K || ldc < N) return NVFP4_ERR_STRIDE;
   if (mode == NVFP4_W4A4) {

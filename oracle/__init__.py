@@ -72,7 +72,11 @@ def _x_args(x: np.ndarray):
         dtype = 1
     else:
         raise TypeError("oracle inputs are float32 or bfloat16 bit patterns (uint16)")
-    if x.ndim != 2 or x.strides[1] != x.itemsize:
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    if x.size == 0:  # empty: no element is read
+        return dtype, x.shape[0], x.shape[1], x.shape[1]
+    if x.strides[1] != x.itemsize:
         raise ValueError("expected a 2-D array with unit stride along K")
     ld = x.strides[0] // x.itemsize
     return dtype, x.shape[0], x.shape[1], ld

@@ -65,7 +65,7 @@ def test_quantize_validation(L):
     assert q(L, S=NULL) == S.ERR_NULL
     assert q(L, dt=7) == S.ERR_DTYPE
     assert q(L, mode=5) == S.ERR_MODE
-    assert q(L, M=0) == S.ERR_SHAPE
+    assert q(L, M=-1) == S.ERR_SHAPE
     assert q(L, K=24, ld=24) == S.ERR_SHAPE
     assert q(L, K=0, ld=0) == S.ERR_SHAPE
     assert q(L, ld=16) == S.ERR_STRIDE
@@ -94,7 +94,7 @@ def test_prepack_validation(L):
     assert L.nvfp4_prepack_weight(NULL, P, 32, 128, P, None) == S.ERR_NULL
     assert L.nvfp4_prepack_weight(P, P, 32, 120, P, None) == S.ERR_SHAPE
     assert L.nvfp4_prepack_weight(P, P, 32, 128, P8, None) == S.ERR_ALIGN
-    assert L.nvfp4_unpack_weight(P, 0, 128, P, P, None) == S.ERR_SHAPE
+    assert L.nvfp4_unpack_weight(P, -1, 128, P, P, None) == S.ERR_SHAPE
 
 
 def g(L, mode=nv.W4A4, a=P, asc=P, ats=P, b=P, bts=P, M=64, N=64, K=128, lda=128, c=P, dt=nv.BF16, ldc=64,
@@ -109,7 +109,8 @@ def test_gemm_validation(L):
     assert g(L, asc=NULL) == S.ERR_NULL
     assert g(L, mode=nv.W4A16) == S.ERR_NULL    # W4A16 must not pass A scales
     assert g(L, dt=4) == S.ERR_DTYPE
-    assert g(L, N=0) == S.ERR_SHAPE
+    assert g(L, N=-1) == S.ERR_SHAPE
+    assert g(L, M=-1) == S.ERR_SHAPE
     assert g(L, K=100, lda=112) == S.ERR_SHAPE
     assert g(L, lda=64) == S.ERR_STRIDE
     assert g(L, ldc=32) == S.ERR_STRIDE
@@ -117,6 +118,24 @@ def test_gemm_validation(L):
     assert g(L, b=P8) == S.ERR_ALIGN
     assert g(L, c=PODD) == S.ERR_ALIGN
     assert g(L, mode=nv.W4A16, asc=NULL, ats=NULL, a=P8) == S.ERR_ALIGN
+
+
+def test_empty_tensors_touch_nothing(L):
+    """M == 0 (or N == 0 for the GEMM and the weight calls) is valid: the call returns OK at once,
+    before any device work, with NULL pointers for the empty arrays.  (Dynamic quantization of an
+    empty tensor still writes S = 0 on the device; the GPU tests cover it.)"""
+    S = nv.Status
+    assert q(L, x=NULL, M=0, packed=NULL, scales=NULL, mode=nv.SCALE_STATIC, ws=NULL, wsb=0) == S.OK
+    assert q(L, x=NULL, M=0, packed=NULL, scales=NULL, S=NULL) == S.ERR_NULL   # S is still needed
+    assert q(L, x=NULL, M=0, K=24, ld=24, mode=nv.SCALE_STATIC) == S.ERR_SHAPE
+    assert L.nvfp4_dequantize(NULL, NULL, NULL, 0, 32, NULL, nv.BF16, 32, None) == S.OK
+    assert L.nvfp4_dequantize(NULL, NULL, NULL, 0, 30, NULL, nv.BF16, 32, None) == S.ERR_SHAPE
+    assert L.nvfp4_prepack_weight(NULL, NULL, 0, 128, NULL, None) == S.OK
+    assert L.nvfp4_unpack_weight(NULL, 0, 128, NULL, NULL, None) == S.OK
+    assert g(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, c=NULL, M=0) == S.OK
+    assert g(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, c=NULL, N=0, ldc=0) == S.OK
+    assert g(L, mode=nv.W4A16, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, c=NULL, M=0) == S.OK
+    assert L.nvfp4_gemm_workspace_bytes(0, 0, 64, 128) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

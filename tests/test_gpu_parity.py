@@ -337,3 +337,36 @@ def test_gemm_w4a16_full_size():
     for name, (w, acts) in workloads.w4a16().items():
         for m, a in acts.items():
             run_w4a16(a, w, torch.bfloat16, sample=None if m <= 16 else 64)
+
+
+def test_empty_tensors():
+    """M == 0: dynamic quantize writes S = 0 (the oracle's maximum over no element), and
+    dequantize / GEMM with an empty side return empty outputs without touching memory."""
+    say("[empty] M=0 quantize / dequantize / gemm, N=0 gemm")
+    K, N = 64, 96
+    x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    S = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
+    p, s, _ = nv.nvfp4_quantize(x, S, static=False)
+    torch.cuda.synchronize()
+    assert p.shape == (0, K // 2) and s.shape == (0, K // 16)
+    assert S.item() == 0.0
+    assert float(oracle.tensor_scale(np.zeros((0, K), np.uint16))) == 0.0
+    y = nv.nvfp4_dequantize(p, s, S, torch.float32)
+    assert y.shape == (0, K)
+    g = torch.Generator().manual_seed(11)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    bp, Sb, _ = prepare_weight(w)
+    out = nv.nvfp4_gemm(nv.W4A4, p, s, S, bp, Sb, N, K, torch.float32)
+    out16 = nv.nvfp4_gemm(nv.W4A16, x, None, None, bp, Sb, N, K, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert out.shape == (0, N) and out16.shape == (0, N)
+    # N == 0: an empty weight
+    xa = torch.randn(5, K, generator=g).to(torch.bfloat16).to(DEV)
+    pa, sa, Sa = nv.nvfp4_quantize(xa)
+    we = torch.empty((0, K // 2), dtype=torch.uint8, device=DEV)
+    se = torch.empty((0, K // 16), dtype=torch.uint8, device=DEV)
+    bpe = nv.nvfp4_prepack_weight(we, se)
+    assert bpe.numel() == 0
+    oute = nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bpe, Sa, 0, K, torch.float32)
+    torch.cuda.synchronize()
+    assert oute.shape == (5, 0)
