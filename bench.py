@@ -290,8 +290,9 @@ def time_graph(fns, side, stream, replays=5):
 
 def hbm_kernels(side, stream):
     """Bandwidth-bound calls at sizes well beyond the 256 MB last-level cache: quantize (dynamic and
-    static) and dequantize of a 32768 x 12288 bf16 tensor, and the weight-only GEMM with M = 1 and
-    16 rows cycling through 32 copies of the prepacked weight (~680 MB)."""
+    static), dequantize and fake quantization (QAT) of a 32768 x 12288 bf16 tensor, and the
+    weight-only GEMM with M = 1 and 16 rows cycling through 32 copies of the prepacked weight
+    (~680 MB)."""
     import torch
 
     import nvfp4_quantized_gemm_amd as nv
@@ -322,6 +323,12 @@ def hbm_kernels(side, stream):
     res[f"quantize_static_bf16_{M}x{K}"] = entry(us, n * (2 + 0.5625))
     us = time_graph([lambda: nv.nvfp4_dequantize(packed, scales, Sst, torch.bfloat16, out=y)] * reps, side, stream)
     res[f"dequantize_bf16_{M}x{K}"] = entry(us, n * (0.5625 + 2))
+    yq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    us = time_graph([lambda: nv.nvfp4_fake_quantize(x, Sst, static=True, out=yq)] * reps, side, stream)
+    res[f"fake_quantize_static_bf16_{M}x{K}"] = entry(us, n * (2 + 2))
+    us = time_graph([lambda: nv.nvfp4_fake_quantize(x, S, static=False, out=yq, workspace=qws)] * reps, side, stream)
+    res[f"fake_quantize_dynamic_bf16_{M}x{K}"] = entry(us, n * (2 + 2 + 2))
+    del yq
     del x, packed, scales, y
     torch.cuda.empty_cache()
 

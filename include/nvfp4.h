@@ -112,6 +112,24 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, co
                                 void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Fake quantization for quantization-aware training [NVFP4-DiT page, Methodology section 2: the
+ * fake-quantize op of QAT, with a straight-through estimator for its gradient; Definition III.1].
+ * Writes y = dequantize(quantize(x)) in one pass, bit-identical to nvfp4_quantize followed by
+ * nvfp4_dequantize with the same S (no NVFP4 tensor is materialized).  The gradient rule (the
+ * straight-through estimator) is the caller's: the Python binding's autograd function passes the
+ * incoming gradient through unchanged.
+ *
+ *   x, x_dtype, M, K, ld_x, tensor_scale, mode, workspace   as for nvfp4_quantize.
+ *   y            device, [M][ld_y] of y_dtype (fp32 or bf16), 16-byte aligned,
+ *                ld_y * sizeof(elem) % 16 == 0, ld_y >= K.  Columns K..ld_y-1 are not written.
+ *   M == 0 is valid (DYNAMIC still writes S = 0).
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_fake_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                   void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, float *tensor_scale,
+                                   nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Weight prepack (offline, once per weight).  Rearranges a canonical NVFP4 weight [N][K]
  * (packed [N][K/2], scales [N][K/16]) into the tile order the GEMM kernels read: N is padded
  * to a multiple of 32 and K to a multiple of 128 with zero codes and zero scales.  The layout is

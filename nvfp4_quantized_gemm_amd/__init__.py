@@ -37,7 +37,7 @@ SCALE_DYNAMIC, SCALE_STATIC = 0, 1
 EXPORTED = (
     "nvfp4_status_string", "nvfp4_abi_version",
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
-    "nvfp4_dequantize",
+    "nvfp4_dequantize", "nvfp4_fake_quantize",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
 )
@@ -69,6 +69,8 @@ def lib():
     L.nvfp4_quantize_workspace_bytes.argtypes = [_i64, _i64]
     L.nvfp4_quantize.restype = _i
     L.nvfp4_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+    L.nvfp4_fake_quantize.restype = _i
+    L.nvfp4_fake_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _i, _i64, _vp, _i, _vp, _sz, _vp]
     L.nvfp4_dequantize.restype = _i
     L.nvfp4_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _i, _i64, _vp]
     L.nvfp4_prepacked_bytes.restype = _sz
@@ -169,6 +171,54 @@ def nvfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor, tensor_scale: t
     return out
 
 
+def nvfp4_fake_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *, static: bool | None = None,
+                        out_dtype: torch.dtype | None = None, out=None, workspace=None, stream=None):
+    """y = dequantize(quantize(x)) in one pass (x [M, K] fp32 or bf16 on the device).  Scale
+    arguments as for nvfp4_quantize.  Returns (y, S)."""
+    M, K, ld = _rows(x, "x")
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype or x.dtype, device=dev)
+    _, _, ld_y = _rows(out, "out")
+    if static is None:
+        static = tensor_scale is not None
+    if tensor_scale is None:
+        if static:
+            raise ValueError("static quantization needs tensor_scale")
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = 0
+    if not static:
+        ws_bytes = nvfp4_quantize_workspace_bytes(M, K)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_fake_quantize(_ptr(x), _dtype_code(x.dtype), M, K, ld, _ptr(out), _dtype_code(out.dtype), ld_y,
+                                   _ptr(tensor_scale), SCALE_STATIC if static else SCALE_DYNAMIC, _ptr(workspace),
+                                   ws_bytes, _stream(stream))
+    _check(st, "nvfp4_fake_quantize")
+    return out, tensor_scale
+
+
+class FakeQuantizeSTE(torch.autograd.Function):
+    """Quantization-aware-training op: forward is NVFP4 fake quantization (nvfp4_fake_quantize, output
+    in x's dtype), backward is the straight-through estimator, i.e. the incoming gradient unchanged."""
+
+    @staticmethod
+    def forward(ctx, x, tensor_scale=None):
+        y, _ = nvfp4_fake_quantize(x.contiguous(), tensor_scale)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        return grad_out, None
+
+
+def fake_quantize_ste(x: torch.Tensor, tensor_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 fake quantization with a straight-through gradient (dynamic scale when tensor_scale is
+    None, else the given static scale)."""
+    return FakeQuantizeSTE.apply(x, tensor_scale)
+
+
 # ---- weight prepack -------------------------------------------------------------------------------
 
 def nvfp4_prepacked_bytes(N: int, K: int) -> int:
@@ -226,7 +276,8 @@ def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked
 __all__ = [
     "Status", "NVFP4Error", "lib", "LIB_PATH", "EXPORTED", "F32", "BF16", "W4A4", "W4A16",
     "SCALE_DYNAMIC", "SCALE_STATIC",
-    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
+    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fake_quantize",
+    "FakeQuantizeSTE", "fake_quantize_ste",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
 ]

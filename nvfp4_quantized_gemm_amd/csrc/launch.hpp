@@ -11,6 +11,10 @@ constexpr int kDequantizeMaxGrid = 4096;
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
                            uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, hipStream_t stream);
+// Fake quantization: y = dequantize(quantize(x)) in one pass (no NVFP4 tensor is written).
+hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, void *y, int y_dtype,
+                                int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
+                                hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
                              int64_t K, void *y, int out_dtype, int64_t ld_y, hipStream_t stream);

@@ -96,6 +96,31 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, i
                                     static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status_t nvfp4_fake_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                   void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, float *tensor_scale,
+                                   nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!tensor_scale) return NVFP4_ERR_NULL;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
+  nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (M > 0 && (!x || !y)) return NVFP4_ERR_NULL;
+  if (M == 0 && mode == NVFP4_SCALE_STATIC) return NVFP4_OK;  // nothing to read or write
+  if (ld_x < K || ld_y < K) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || ((ld_x * elem_size(x_dtype)) % 16) != 0 || !aligned(y, 16) ||
+      ((ld_y * elem_size(y_dtype)) % 16) != 0 || !aligned(tensor_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  if (mode == NVFP4_SCALE_DYNAMIC) {
+    if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_fake_quantize(x, (int)x_dtype, M, K, ld_x, y, (int)y_dtype, ld_y, tensor_scale,
+                                         mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
+                                         static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
                                 int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;

@@ -182,6 +182,50 @@ __device__ __forceinline__ uint32_t block_byte(float amax, float S, float rlo, f
   return scale_byte_exact(amax, S);
 }
 
+// Fake quantization output: the lane's E codes dequantized exactly as the dequantize kernel does,
+// y = RN32((q * e) * S) with q * e exact, then bf16 (nearest, ties to even) for YT = 1.
+template <int E, int YT>
+__device__ __forceinline__ void store_fake(uint32_t codes, uint32_t byte, float S, void *y, uint64_t off) {
+  const float e = e4m3_to_f32(byte);
+  float out[E];
+  const f32x2 q0 = fp4_decode2_f32<0>(codes), q1 = fp4_decode2_f32<1>(codes);
+  out[0] = (q0.x * e) * S;
+  out[1] = (q0.y * e) * S;
+  out[2] = (q1.x * e) * S;
+  out[3] = (q1.y * e) * S;
+  if (E == 8) {
+    const f32x2 q2 = fp4_decode2_f32<2>(codes), q3 = fp4_decode2_f32<3>(codes);
+    out[4] = (q2.x * e) * S;
+    out[5] = (q2.y * e) * S;
+    out[6] = (q3.x * e) * S;
+    out[7] = (q3.y * e) * S;
+  }
+  if (YT == 0) {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off);
+#pragma unroll
+    for (int h = 0; h < E / 4; ++h) {
+      const u32x4 o = {__float_as_uint(out[4 * h]), __float_as_uint(out[4 * h + 1]), __float_as_uint(out[4 * h + 2]),
+                       __float_as_uint(out[4 * h + 3])};
+      dst[h] = o;
+    }
+  } else {
+    uint32_t p[E / 2];
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const bf16x2 hh = {(__bf16)out[2 * j], (__bf16)out[2 * j + 1]};
+      p[j] = __builtin_bit_cast(uint32_t, hh);
+    }
+    uint16_t *dst = static_cast<uint16_t *>(y) + off;
+    if (E == 8) {
+      const u32x4 o = {p[0], p[1], p[2], p[3]};
+      *reinterpret_cast<u32x4 *>(dst) = o;
+    } else {
+      const u32x2 o = {p[0], p[1]};
+      *reinterpret_cast<u32x2 *>(dst) = o;
+    }
+  }
+}
+
 // ---- dynamic amax: per-workgroup partial maxima ------------------------------------------------------
 
 template <int DT, bool DENSE>
@@ -216,11 +260,15 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
 
 // ---- quantize ------------------------------------------------------------------------------------
 
-template <int DT, bool DYNAMIC, bool DENSE>
+// YT < 0: write the NVFP4 tensor (packed codes + scale bytes).  YT = 0 / 1: fake quantization,
+// write dequantize(quantize(x)) as fp32 / bf16 into y [.][ld_y] instead (one pass, same values as
+// the two calls).
+template <int DT, bool DYNAMIC, bool DENSE, int YT>
 __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                                   FastDiv bpr, uint8_t *__restrict__ packed,
                                                   uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
-                                                  const float *__restrict__ partial, int npartial) {
+                                                  const float *__restrict__ partial, int npartial,
+                                                  void *__restrict__ y, int64_t ld_y) {
   using In = SegIn<DT>;
   constexpr int E = In::kElems;
   using Map = Segments<E>;
@@ -296,9 +344,13 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
       } else {
         codes = encode_values<E>(v, byte, S, invS, fast_ok, ties_only);
       }
-      if (E == 8) *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
-      else *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
-      if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)byte;
+      if (YT < 0) {
+        if (E == 8) *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
+        else *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
+        if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)byte;
+      } else {
+        store_fake<E, YT>(codes, byte, S, y, Map::template offset<DENSE>(g, bpr, ld_y));
+      }
     }
   }
 }
@@ -312,16 +364,33 @@ static int grid_for(uint64_t nseg, int cap) {
   return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
 }
 
-template <int DT, bool DENSE>
+template <int DT, bool DENSE, int YT>
 static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr, uint8_t *packed, uint8_t *scales,
-                         float *tensor_scale, bool dynamic, float *partial, hipStream_t stream) {
+                         float *tensor_scale, bool dynamic, float *partial, void *y, int64_t ld_y,
+                         hipStream_t stream) {
   const int gq = grid_for(nseg, kQuantizeMaxGrid);
   if (dynamic) {
     const int ga = grid_for(nseg, kAmaxPartials);
     k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr, partial);
-    k_quantize<DT, true, DENSE><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, partial, ga);
+    k_quantize<DT, true, DENSE, YT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, partial,
+                                                            ga, y, ld_y);
   } else {
-    k_quantize<DT, false, DENSE><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, nullptr, 0);
+    k_quantize<DT, false, DENSE, YT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
+                                                             nullptr, 0, y, ld_y);
+  }
+}
+
+template <int YT>
+static void dispatch_quantize(const void *x, int dtype, int64_t K, int64_t ld, uint64_t nseg, FastDiv bpr,
+                              uint8_t *packed, uint8_t *scales, float *tensor_scale, bool dynamic, float *partial,
+                              void *y, int64_t ld_y, hipStream_t stream) {
+  const bool dense = (ld == K) && (YT < 0 || ld_y == K);
+  if (dtype == 0) {
+    if (dense) run_quantize<0, true, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
+    else run_quantize<0, false, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
+  } else {
+    if (dense) run_quantize<1, true, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
+    else run_quantize<1, false, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
   }
 }
 
@@ -330,14 +399,19 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64
                            hipStream_t stream) {
   const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
   const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
-  const bool dense = (ld == K);
-  if (dtype == 0) {
-    if (dense) run_quantize<0, true>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
-    else run_quantize<0, false>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
-  } else {
-    if (dense) run_quantize<1, true>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
-    else run_quantize<1, false>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, stream);
-  }
+  dispatch_quantize<-1>(x, dtype, K, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, nullptr, 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, void *y, int y_dtype,
+                                int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
+                                hipStream_t stream) {
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
+  if (y_dtype == 0)
+    dispatch_quantize<0>(x, dtype, K, ld, nseg, bpr, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, stream);
+  else
+    dispatch_quantize<1>(x, dtype, K, ld, nseg, bpr, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, stream);
   return hipGetLastError();
 }
 

@@ -89,6 +89,24 @@ def test_dequantize_validation(L):
     assert d(ld=33) == S.ERR_ALIGN
 
 
+def test_fake_quantize_validation(L):
+    S = nv.Status
+    f = lambda **kw: L.nvfp4_fake_quantize(kw.get("x", P), kw.get("dt", nv.BF16), kw.get("M", 4), kw.get("K", 32),
+                                           kw.get("ld", 32), kw.get("y", P), kw.get("ydt", nv.F32),
+                                           kw.get("ldy", 32), kw.get("S", P), kw.get("mode", nv.SCALE_DYNAMIC),
+                                           kw.get("ws", P), kw.get("wsb", 4096), None)
+    assert f(S=NULL) == S.ERR_NULL
+    assert f(y=NULL) == S.ERR_NULL
+    assert f(ydt=9) == S.ERR_DTYPE
+    assert f(mode=3) == S.ERR_MODE
+    assert f(K=40, ld=40, ldy=40) == S.ERR_SHAPE
+    assert f(ldy=16) == S.ERR_STRIDE
+    assert f(y=P8) == S.ERR_ALIGN
+    assert f(ydt=nv.BF16, ldy=36) == S.ERR_ALIGN
+    assert f(ws=NULL) == S.ERR_WORKSPACE
+    assert f(x=NULL, y=NULL, M=0, mode=nv.SCALE_STATIC, ws=NULL, wsb=0) == S.OK
+
+
 def test_prepack_validation(L):
     S = nv.Status
     assert L.nvfp4_prepack_weight(NULL, P, 32, 128, P, None) == S.ERR_NULL

@@ -370,3 +370,77 @@ def test_empty_tensors():
     oute = nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bpe, Sa, 0, K, torch.float32)
     torch.cuda.synchronize()
     assert oute.shape == (5, 0)
+
+
+# ---- fake quantization (QAT) ------------------------------------------------------------------------
+
+def oracle_fake(x_cpu, static_S, out_dtype):
+    op, os_, oS = oracle.quantize(np_x(x_cpu), S=static_S)
+    y32, y16 = oracle.dequantize(op, os_, oS)
+    return (y32.view(np.uint32) if out_dtype == torch.float32 else y16), oS
+
+
+def run_fake(x_cpu, static_S, out_dtype, ld_x=None, ld_y=None, label=""):
+    M, K = x_cpu.shape
+    say(f"[fake] {label} {tuple(x_cpu.shape)} {x_cpu.dtype}->{out_dtype} static={static_S} ld={ld_x},{ld_y}")
+    if ld_x is not None and ld_x != K:
+        big = torch.full((M, ld_x), 1e30, dtype=x_cpu.dtype)
+        big[:, :K] = x_cpu
+        xd = big.to(DEV)[:, :K]
+    else:
+        xd = x_cpu.to(DEV)
+    esz = 4 if out_dtype == torch.float32 else 2
+    ld_y = ld_y or K
+    gy = Guarded(M * ld_y * esz)
+    yb = gy.payload((M, ld_y), out_dtype)
+    yb.fill_(7.0)
+    y = yb[:, :K]
+    Sd = (torch.tensor([static_S], dtype=torch.float32, device=DEV) if static_S is not None
+          else torch.empty(1, dtype=torch.float32, device=DEV))
+    nv.nvfp4_fake_quantize(xd, Sd, static=static_S is not None, out=y)
+    torch.cuda.synchronize()
+    gy.check()
+    assert (yb[:, K:] == 7.0).all(), "padding columns of y written"
+    want, oS = oracle_fake(x_cpu, static_S, out_dtype)
+    assert np.float32(Sd.item()).view(np.uint32) == np.float32(oS).view(np.uint32)
+    got = y.cpu().contiguous()
+    got = got.view(torch.int32).numpy().view(np.uint32) if out_dtype == torch.float32 else np_bf16(got)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} outputs differ, first at {bad[0][0], bad[1][0]}"
+    return y
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_fake_quantize_sweep(out_dtype):
+    x = workloads.sweep(4096, 1152)
+    run_fake(x, None, out_dtype, label="sweep dynamic")
+    xs = workloads.sweep(4096, 1152, static=True)
+    run_fake(xs, workloads.SWEEP_STATIC_S, out_dtype, label="sweep static")
+
+
+@pytest.mark.parametrize("M,K,ld_x,ld_y,dt,out", [
+    (1, 16, 16, 16, torch.float32, torch.float32), (37, 48, 56, 64, torch.bfloat16, torch.float32),
+    (255, 1168, 1168, 1176, torch.float32, torch.bfloat16), (300, 272, 280, 272, torch.bfloat16, torch.bfloat16),
+])
+def test_fake_quantize_ragged(M, K, ld_x, ld_y, dt, out):
+    g = torch.Generator().manual_seed(M + K)
+    x = (torch.randn(M, K, generator=g) * torch.exp(2 * torch.randn(M, 1, generator=g))).to(dt)
+    run_fake(x, None, out, ld_x, ld_y, label="ragged dynamic")
+    run_fake(x, 0.004, out, ld_x, ld_y, label="ragged static")
+
+
+def test_fake_quantize_equals_quantize_then_dequantize_and_ste():
+    x, _ = workloads.tiny()
+    xd = x.to(DEV)
+    p, s, S = nv.nvfp4_quantize(xd)
+    y2 = nv.nvfp4_dequantize(p, s, S, torch.float32)
+    y1, S1 = nv.nvfp4_fake_quantize(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)) and S1.item() == S.item()
+    # straight-through estimator: the gradient passes unchanged
+    xg = xd.clone().requires_grad_(True)
+    yg = nv.fake_quantize_ste(xg)
+    assert torch.equal(yg.detach().view(torch.int32), y1.view(torch.int32))
+    gout = torch.randn_like(xg)
+    yg.backward(gout)
+    assert torch.equal(xg.grad, gout)
