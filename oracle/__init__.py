@@ -49,6 +49,14 @@ def _load():
     lib.ora_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, ctypes.c_int]
     lib.ora_dequantize.restype = ctypes.c_int
     lib.ora_dequantize.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp, ctypes.c_int]
+    lib.ora_mx_scale_byte.restype = ctypes.c_int
+    lib.ora_mx_scale_byte.argtypes = [ctypes.c_double]
+    lib.ora_mx_element_code.restype = ctypes.c_int
+    lib.ora_mx_element_code.argtypes = [ctypes.c_float, ctypes.c_int]
+    lib.ora_mx_quantize.restype = ctypes.c_int
+    lib.ora_mx_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, ctypes.c_int]
+    lib.ora_mx_dequantize.restype = ctypes.c_int
+    lib.ora_mx_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_int]
     lib.ora_gemm.restype = ctypes.c_int
     lib.ora_gemm.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, ctypes.c_int]
     lib.ora_gemm_sampled.restype = ctypes.c_int
@@ -146,6 +154,44 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, S, threads: int | None = 
     y16 = np.empty((M, K), np.uint16)
     rc = _load().ora_dequantize(_ptr(packed), _ptr(scales), float(np.float32(S)), M, K, _ptr(y32), _ptr(y16),
                                 threads or default_threads())
+    if rc != 0:
+        raise ValueError("precondition failed")
+    return y32, y16
+
+
+# ---- MXFP4 (OCP microscaling: 32-value blocks, E8M0 scales, no tensor scale) ---------------------
+
+def mx_scale_byte(amax: float) -> int:
+    return _load().ora_mx_scale_byte(float(amax))
+
+
+def mx_element_code(v, byte: int) -> int:
+    return _load().ora_mx_element_code(float(np.float32(v)), int(byte))
+
+
+def mx_quantize(x: np.ndarray, threads: int | None = None):
+    """MXFP4-quantize x [M, K] (K % 32 == 0).  Returns (packed uint8 [M, K/2], scales uint8 [M, K/32])."""
+    dtype, M, K, ld = _x_args(x)
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    packed = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M, K // 32), np.uint8)
+    rc = _load().ora_mx_quantize(_ptr(x), dtype, M, K, ld, _ptr(packed), _ptr(scales), threads or default_threads())
+    if rc != 0:
+        raise ValueError("precondition failed (non-finite input)")
+    return packed, scales
+
+
+def mx_dequantize(packed: np.ndarray, scales: np.ndarray, threads: int | None = None):
+    """Returns (y_f32 float32 [M, K], y_bf16 uint16 [M, K])."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    M, K = packed.shape[0], packed.shape[1] * 2
+    if scales.shape != (M, K // 32):
+        raise ValueError("scales shape does not match packed")
+    y32 = np.empty((M, K), np.float32)
+    y16 = np.empty((M, K), np.uint16)
+    rc = _load().ora_mx_dequantize(_ptr(packed), _ptr(scales), M, K, _ptr(y32), _ptr(y16), threads or default_threads())
     if rc != 0:
         raise ValueError("precondition failed")
     return y32, y16

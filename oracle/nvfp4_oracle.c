@@ -212,6 +212,92 @@ int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_
   return bad ? -1 : 0;
 }
 
+/* ---- MXFP4 ---------------------------------------------------------------------------------
+ *
+ * The vllm-omni RFC (Motivation) names MXFP4 as the related microscaling format but does not
+ * define it; these functions follow the public OCP Microscaling (MX) format definition:
+ *   - blocks of 32 consecutive values along K share one E8M0 scale X = 2^(b - 127), b a byte
+ *     (255 would be NaN and is never produced);
+ *   - X = 2^(floor(log2 amax) - 2), 2 being the largest E2M1 exponent, so amax / X lies in
+ *     [4, 8); b is clamped to [0, 254], and an all-zero block gets b = 0;
+ *   - each value becomes the E2M1 value nearest to v / X (ties to the even code, clipped to +-6),
+ *     sign bit copied; there is no per-tensor scale;
+ *   - dequantize: y = RN32(q * X), which is exact for every scale byte the quantizer produces
+ *     from finite fp32 / bf16 input (b <= 252); larger bytes can round to +-inf.
+ * Packing is the same as NVFP4 (element 2i in the low nibble of byte i); scales are [M][K/32].
+ */
+int ora_mx_scale_byte(double amax) {
+  if (amax == 0.0) return 0;
+  int e;
+  (void)frexp(amax, &e); /* amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  int b = (e - 1) - 2 + 127;
+  return b < 0 ? 0 : (b > 254 ? 254 : b);
+}
+
+int ora_mx_element_code(float v, int byte) {
+  double X = ldexp(1.0, byte - 127);
+  double a = fabs((double)v);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < 8; ++c) { /* nearest of the 8 magnitudes; on a tie keep the even code */
+    double d = fabs(a - ora_e2m1_value(c) * X);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return best | (signbit(v) ? 8 : 0);
+}
+
+int ora_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+                    uint8_t *scales, int nthreads) {
+  if (K % 32 != 0 || ld < K) return -1;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16) reduction(| : bad)
+#endif
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < K / 32; ++j) {
+      float v[32];
+      double amax = 0.0;
+      for (int t = 0; t < 32; ++t) {
+        v[t] = load_x(x, dtype, i * ld + 32 * j + t);
+        if (!isfinite(v[t])) bad = 1;
+        if (fabs((double)v[t]) > amax) amax = fabs((double)v[t]);
+      }
+      int byte = ora_mx_scale_byte(amax);
+      scales[i * (K / 32) + j] = (uint8_t)byte;
+      for (int t = 0; t < 32; t += 2) {
+        int c0 = ora_mx_element_code(v[t], byte), c1 = ora_mx_element_code(v[t + 1], byte);
+        packed[i * (K / 2) + 16 * j + t / 2] = (uint8_t)(c0 | (c1 << 4));
+      }
+    }
+  }
+  return bad ? -1 : 0;
+}
+
+int ora_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, float *y_f32,
+                      uint16_t *y_bf16, int nthreads) {
+  if (K % 32 != 0) return -1;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16) reduction(| : bad)
+#endif
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t k = 0; k < K; ++k) {
+      int byte = scales[i * (K / 32) + k / 32];
+      if (byte == 255) bad = 1;
+      int code = (packed[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+      float y = (float)(ora_e2m1_value(code) * ldexp(1.0, byte - 127)); /* exact */
+      if (y_f32) y_f32[i * K + k] = y;
+      if (y_bf16) y_bf16[i * K + k] = ora_bf16_round(y);
+    }
+  }
+  return bad ? -1 : 0;
+}
+
 /* ---- GEMM --------------------------------------------------------------------------------- */
 
 int ora_gemm(const float *A, int64_t lda, const float *B, int64_t ldb, int64_t M, int64_t N, int64_t K,

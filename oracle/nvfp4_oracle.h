@@ -40,6 +40,15 @@ int ora_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, flo
 int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K,
                    float *y_f32, uint16_t *y_bf16, int nthreads);
 
+/* MXFP4 (OCP microscaling): 32-value blocks, E8M0 scale X = 2^(floor(log2 amax) - 2), no tensor
+   scale; scales are [M][K/32] bytes. */
+int ora_mx_scale_byte(double amax);
+int ora_mx_element_code(float v, int byte);
+int ora_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+                    uint8_t *scales, int nthreads);
+int ora_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, float *y_f32,
+                      uint16_t *y_bf16, int nthreads);
+
 /* Y[i][j] = sum_k A[i][k]*B[j][k] accumulated in fp64; R[i][j] = sum_k |A[i][k]*B[j][k]|. */
 int ora_gemm(const float *A, int64_t lda, const float *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
              double *Y, double *R, int nthreads);
