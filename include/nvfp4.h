@@ -168,6 +168,33 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
                           int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * MXFP4, the related microscaling format (vllm-omni RFC, Motivation; the pages do not define it,
+ * the OCP microscaling definition is followed): blocks of 32 consecutive values along K share one
+ * E8M0 scale byte b (X = 2^(b - 127)), X = 2^(floor(log2 amax) - 2) with b clamped to [0, 254] and
+ * b = 0 for an all-zero block; each value is the E2M1 code nearest to v / X (ties to the even code,
+ * clipped to +-6, sign copied); there is no tensor scale.  Codes are packed as for NVFP4 (element 2i
+ * in the low nibble of byte i, [M][K/2]); scales are [M][K/32] bytes.  K >= 32, K % 32 == 0,
+ * M == 0 is valid and touches nothing.
+ *
+ * nvfp4_mx_quantize    x as for nvfp4_quantize (fp32 or bf16, 16-byte aligned rows); packed
+ *                      8-byte aligned.  Bit-identical to the definition for every finite input.
+ * nvfp4_mx_dequantize  y = q * X (exact for every byte the quantizer produces); bf16 output is
+ *                      the nearest bf16 of it.  y as for nvfp4_dequantize.
+ * nvfp4_mx_gemm        Y = A * B^T with A [M][K] and B [N][K] both canonical MXFP4 (a, b 16-byte
+ *                      aligned; a_scales, b_scales 4-byte aligned), on the block-scaled FP4 matrix
+ *                      instruction: the products are exact in fp32 and accumulate in fp32, so only
+ *                      the summation order differs from dequantize-then-matmul.  c as for
+ *                      nvfp4_gemm (fp32 or bf16, base 16-byte aligned, ldc >= N).  N == 0 is valid.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_mx_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 uint8_t *packed, uint8_t *scales, void *stream);
+nvfp4_status_t nvfp4_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, void *y,
+                                   nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream);
+nvfp4_status_t nvfp4_mx_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b, const uint8_t *b_scales,
+                             int64_t M, int64_t N, int64_t K, void *c, nvfp4_dtype_t c_dtype, int64_t ldc,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

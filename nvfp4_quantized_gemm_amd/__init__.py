@@ -40,6 +40,7 @@ EXPORTED = (
     "nvfp4_dequantize", "nvfp4_fake_quantize",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
 )
 
 _lib = None
@@ -83,6 +84,12 @@ def lib():
     L.nvfp4_gemm_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
     L.nvfp4_gemm.restype = _i
     L.nvfp4_gemm.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _i64, _vp, _sz, _vp]
+    L.nvfp4_mx_quantize.restype = _i
+    L.nvfp4_mx_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _vp, _vp]
+    L.nvfp4_mx_dequantize.restype = _i
+    L.nvfp4_mx_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _i, _i64, _vp]
+    L.nvfp4_mx_gemm.restype = _i
+    L.nvfp4_mx_gemm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i, _i64, _vp]
     _lib = L
     return L
 
@@ -273,6 +280,43 @@ def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked
     return out
 
 
+# ---- MXFP4 (32-value blocks, E8M0 scales, no tensor scale) ------------------------------------
+
+def nvfp4_mx_quantize(x: torch.Tensor, *, packed=None, scales=None, stream=None):
+    """MXFP4-quantize x [M, K] (fp32 or bf16, K % 32 == 0).  Returns (packed u8 [M, K/2], scales u8 [M, K/32])."""
+    M, K, ld = _rows(x, "x")
+    if packed is None:
+        packed = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, max(K // 32, 0)), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_mx_quantize(_ptr(x), _dtype_code(x.dtype), M, K, ld, _ptr(packed), _ptr(scales), _stream(stream)),
+           "nvfp4_mx_quantize")
+    return packed, scales
+
+
+def nvfp4_mx_dequantize(packed: torch.Tensor, scales: torch.Tensor, dtype: torch.dtype = torch.float32, *, out=None,
+                        stream=None) -> torch.Tensor:
+    M, K = packed.shape[0], packed.shape[1] * 2
+    if out is None:
+        out = torch.empty((M, K), dtype=dtype, device=packed.device)
+    _, _, ld = _rows(out, "out")
+    _check(lib().nvfp4_mx_dequantize(_ptr(packed), _ptr(scales), M, K, _ptr(out), _dtype_code(out.dtype), ld,
+                                     _stream(stream)), "nvfp4_mx_dequantize")
+    return out
+
+
+def nvfp4_mx_gemm(a: torch.Tensor, a_scales: torch.Tensor, b: torch.Tensor, b_scales: torch.Tensor,
+                  out_dtype: torch.dtype = torch.bfloat16, *, out=None, stream=None) -> torch.Tensor:
+    """Y = A B^T with A [M, K] and B [N, K] both canonical MXFP4 (packed codes + E8M0 scales)."""
+    M, K = a.shape[0], a.shape[1] * 2
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(lib().nvfp4_mx_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), M, N, K, _ptr(out),
+                               _dtype_code(out.dtype), out.stride(0), _stream(stream)), "nvfp4_mx_gemm")
+    return out
+
+
 __all__ = [
     "Status", "NVFP4Error", "lib", "LIB_PATH", "EXPORTED", "F32", "BF16", "W4A4", "W4A16",
     "SCALE_DYNAMIC", "SCALE_STATIC",
@@ -280,4 +324,5 @@ __all__ = [
     "FakeQuantizeSTE", "fake_quantize_ste",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
 ]

@@ -77,16 +77,44 @@ __device__ __forceinline__ float swap_lane2(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
-// Lane-contiguous element mapping of the bandwidth kernels.  A tensor of M rows x K (K % 16 == 0)
-// is cut into segments of EPL consecutive elements along K, numbered row-major; EPL is chosen so
-// that a segment is 16 bytes of the wide side (8 bf16 or 4 fp32), and consecutive lanes take
-// consecutive segments, so every wave-wide load or store covers one contiguous span.  Segment g
-// lies in 16-value block g / LPB (LPB = 16 / EPL adjacent lanes share a block).
-template <int EPL>
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS copies (gfx950 LDS-DMA): every lane supplies its own global address; the
+// wave's data lands contiguously at `lds` (lane i at lds + i * size).  `lds` must be wave-uniform.
+__device__ __forceinline__ void g2l16(const void *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l4(const void *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are outstanding (they complete in
+// issue order), then meet the other waves at a bare barrier: unlike __syncthreads() this does not
+// also wait for the loads issued after the ones needed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Lane swap across quads: lane i reads lane i ^ 4 (ds_swizzle bit mode, xor mask 4).
+__device__ __forceinline__ float swap_lane4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+
+// Lane-contiguous element mapping of the bandwidth kernels.  A tensor of M rows x K (K a multiple
+// of the block size BLK) is cut into segments of EPL consecutive elements along K, numbered
+// row-major; EPL is chosen so that a segment is 16 bytes of the wide side (8 bf16 or 4 fp32), and
+// consecutive lanes take consecutive segments, so every wave-wide load or store covers one
+// contiguous span.  Segment g lies in block g / LPB (LPB = BLK / EPL adjacent lanes share a block).
+template <int EPL, int BLK = 16>
 struct Segments {
-  static constexpr int kLanesPerBlock = 16 / EPL;
-  static constexpr int kShift = (kLanesPerBlock == 2) ? 1 : 2;
+  static constexpr int kLanesPerBlock = BLK / EPL;
+  static constexpr int kShift = (kLanesPerBlock == 2) ? 1 : (kLanesPerBlock == 4) ? 2 : 3;
   static_assert(EPL == 8 || EPL == 4, "segments are 8 or 4 elements");
+  static_assert(kLanesPerBlock == 2 || kLanesPerBlock == 4 || kLanesPerBlock == 8, "lanes per block");
   // element offset of segment g in a tensor with row stride ld (elements); rows of exactly K
   // elements (DENSE) need no division, otherwise bpr divides by the blocks per row
   template <bool DENSE>
@@ -94,8 +122,43 @@ struct Segments {
     if (DENSE) return g * EPL;
     const uint32_t blk = (uint32_t)(g >> kShift);
     const uint32_t row = fastdiv(blk, bpr);
-    const uint32_t col = (blk - row * bpr.d) * 16u + (uint32_t)(g & (kLanesPerBlock - 1)) * EPL;
+    const uint32_t col = (blk - row * bpr.d) * BLK + (uint32_t)(g & (kLanesPerBlock - 1)) * EPL;
     return (uint64_t)row * (uint64_t)ld + col;
+  }
+};
+
+// Input loading of the bandwidth kernels: one 16-byte segment per lane (raw), then unpacked to fp32.
+
+template <int DT>
+struct SegIn;
+
+template <>
+struct SegIn<0> {  // fp32: 4 values
+  static constexpr int kElems = 4;
+  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
+    return *reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem_off);
+  }
+  __device__ static void unpack(const u32x4 &w, float v[4]) {
+    v[0] = __uint_as_float(w.x);
+    v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z);
+    v[3] = __uint_as_float(w.w);
+  }
+};
+
+template <>
+struct SegIn<1> {  // bf16: 8 values
+  static constexpr int kElems = 8;
+  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
+    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem_off);
+  }
+  __device__ static void unpack(const u32x4 &w, float v[8]) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[2 * t] = bf16lo(a[t]);
+      v[2 * t + 1] = bf16hi(a[t]);
+    }
   }
 };
 

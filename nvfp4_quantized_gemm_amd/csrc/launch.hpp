@@ -59,4 +59,12 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *p
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
                                 int64_t ldc, const float *a_ts, const float *b_ts, hipStream_t stream);
 
+// MXFP4 (mxfp4.hip): 32-value blocks with E8M0 scales, GEMM on the block-scaled FP4 MFMA.
+hipError_t launch_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+                              uint8_t *scales, hipStream_t stream);
+hipError_t launch_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, void *y,
+                                int out_dtype, int64_t ld_y, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
+                          int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -1,0 +1,411 @@
+// MXFP4 for gfx950: 32-value blocks with a power-of-two E8M0 scale (the OCP microscaling format;
+// the vllm-omni NVFP4 RFC names MXFP4 as the related format, Motivation).  Quantize, dequantize and
+// a GEMM on CDNA4's block-scaled FP4 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// Definition: per block, X = 2^(floor(log2 amax) - 2) clamped to 2^-127 (byte 0 also for an
+// all-zero block); each value becomes the E2M1 value nearest to v / X, ties to the even code,
+// clipped to +-6, sign copied.  With b the E8M0 byte, floor(log2 amax) + 127 is amax's exponent
+// field E, so b = max(E - 2, 0); v * 2^(127 - b) is exact (a power-of-two scaling whose result is
+// below 8), and the hardware E2M1 conversion (round-half-even, saturating, sign-preserving) of that
+// exact value is the code: no bracketing is needed.  Dequantize: y = q * 2^(b - 127), exact in fp32
+// for every byte the quantizer produces.
+//
+// GEMM: the matrix instruction takes, per lane l (row l % 32, k-half l / 32 of a 64-k step), 16
+// bytes holding 32 E2M1 codes low nibble first -- exactly 16 contiguous bytes of a canonical packed
+// row -- and one E8M0 byte per lane (its row's 32-value block) selected by op_sel.  Both operands
+// are therefore streamed straight from the canonical layout into LDS by LDS-DMA; no prepack and no
+// dequantization.  The products q_a X_a q_b X_b are exact in fp32 and accumulate in fp32.
+#include <type_traits>
+
+#include "common.hpp"
+#include "epilogue.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kMxBlk = 32;
+constexpr int kMxSegsPerLane = 4;
+
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {  // amax >= 0, finite
+  const uint32_t E = (__float_as_uint(amax) >> 23) & 0xffu;
+  return E >= 2u ? E - 2u : 0u;
+}
+// 2^(127 - b) for b <= 252: maps the block onto the E2M1 grid exactly
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
+// X = 2^(b - 127) as fp32 (2^-127 is the subnormal 0x00400000)
+__device__ __forceinline__ float mx_scale_value(uint32_t b) { return __uint_as_float(b ? (b << 23) : 0x00400000u); }
+
+int mx_grid(uint64_t nseg, int cap) {
+  const uint64_t tiles = (nseg + 64 * kMxSegsPerLane - 1) / (64 * kMxSegsPerLane);
+  uint64_t g = (tiles + 3) / 4;
+  if (g < 1) g = 1;
+  return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
+}
+
+}  // namespace
+
+// ---- quantize: lane-contiguous 16-byte segments, 4 (bf16) or 8 (fp32) lanes per 32-value block ----
+
+template <int DT, bool DENSE>
+__global__ __launch_bounds__(256) void k_mx_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
+                                                     FastDiv bpr, uint8_t *__restrict__ packed,
+                                                     uint8_t *__restrict__ scales) {
+  using In = SegIn<DT>;
+  constexpr int E = In::kElems;
+  using Map = Segments<E, kMxBlk>;
+  constexpr int U = kMxSegsPerLane;
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
+  const uint64_t tstride = gridDim.x * 4ull;
+  auto fetch = [&](uint64_t t, u32x4 *r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;
+      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
+    }
+  };
+  uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
+  u32x4 nxt[U];
+  if (t < ntiles) fetch(t, nxt);
+  for (; t < ntiles; t += tstride) {
+    u32x4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    if (t + tstride < ntiles) fetch(t + tstride, nxt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = t * (64 * U) + u * 64 + lane;
+      float v[E];
+      In::unpack(cur[u], v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      amax = fmaxf(amax, swap_lane1(amax));
+      amax = fmaxf(amax, swap_lane2(amax));
+      if (Map::kLanesPerBlock == 8) amax = fmaxf(amax, swap_lane4(amax));
+      if (g >= nseg) continue;  // whole blocks are in or out of range
+      const uint32_t b = mx_scale_byte(amax);
+      const float m = mx_inv_scale(b);
+      uint32_t codes = 0;
+      codes = fp4_encode2<0>(codes, v[0] * m, v[1] * m);
+      codes = fp4_encode2<1>(codes, v[2] * m, v[3] * m);
+      if (E == 8) {
+        codes = fp4_encode2<2>(codes, v[4] * m, v[5] * m);
+        codes = fp4_encode2<3>(codes, v[6] * m, v[7] * m);
+        *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
+      } else {
+        *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
+      }
+      if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)b;
+    }
+  }
+}
+
+// ---- dequantize: y = q * X ----------------------------------------------------------------------------
+
+template <int OUT, bool DENSE>
+__global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict__ packed,
+                                                       const uint8_t *__restrict__ scales, uint64_t nseg,
+                                                       FastDiv bpr, void *__restrict__ y, int64_t ld_y) {
+  constexpr int E = (OUT == 1) ? 8 : 4;
+  using Map = Segments<E, kMxBlk>;
+  constexpr int U = kMxSegsPerLane;
+  const int lane = threadIdx.x & 63;
+  const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
+  for (uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6); t < ntiles; t += gridDim.x * 4ull) {
+    uint32_t codes[U], sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint64_t g = t * (64 * U) + u * 64 + lane;
+      g = g < nseg ? g : nseg - 1;
+      codes[u] = (E == 8) ? *reinterpret_cast<const uint32_t *>(packed + 4 * g)
+                          : (uint32_t) * reinterpret_cast<const uint16_t *>(packed + 2 * g);
+      sb[u] = scales[g >> Map::kShift];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = t * (64 * U) + u * 64 + lane;
+      if (g >= nseg) break;
+      const float X = mx_scale_value(sb[u]);
+      float out[E];
+      const f32x2 q0 = fp4_decode2_f32<0>(codes[u]), q1 = fp4_decode2_f32<1>(codes[u]);
+      out[0] = q0.x * X;
+      out[1] = q0.y * X;
+      out[2] = q1.x * X;
+      out[3] = q1.y * X;
+      if (E == 8) {
+        const f32x2 q2 = fp4_decode2_f32<2>(codes[u]), q3 = fp4_decode2_f32<3>(codes[u]);
+        out[4] = q2.x * X;
+        out[5] = q2.y * X;
+        out[6] = q3.x * X;
+        out[7] = q3.y * X;
+      }
+      const uint64_t off = Map::template offset<DENSE>(g, bpr, ld_y);
+      u32x4 o;
+      if (OUT == 0) {
+        o.x = __float_as_uint(out[0]);
+        o.y = __float_as_uint(out[1]);
+        o.z = __float_as_uint(out[2]);
+        o.w = __float_as_uint(out[3]);
+        *reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off) = o;
+      } else {
+        uint32_t p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 h = {(__bf16)out[2 * j], (__bf16)out[2 * j + 1]};
+          p[j] = __builtin_bit_cast(uint32_t, h);
+        }
+        o.x = p[0];
+        o.y = p[1];
+        o.z = p[2];
+        o.w = p[3];
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + off) = o;
+      }
+    }
+  }
+}
+
+// ---- GEMM: Y[M][N] = A[M][K] B[N][K]^T, both operands canonical MXFP4 ---------------------------------
+//
+// 256x256 tile per 256-thread workgroup (2 x 2 waves of 128 x 128 = 4 x 4 tiles of 32 x 32), K in
+// chunks of 128 (two 64-k MFMA steps).  LDS stage (36 KB):
+//   A codes  [8 row groups][2 steps][64 lanes][16 B]   A scales [8 row groups][64 lanes][4 B]
+//   B codes, B scales likewise (column groups).
+// Lane (r, h) of a codes block holds row 32 grp + r, bytes 32 step + 16 h of the chunk (k-half h of
+// the step); lane l of a scales block holds its row's 4 scale bytes of the chunk (block 2 step + h of
+// them is the one it feeds to the MFMA: the lane shifts the word right by 8 h and op_sel picks byte
+// 2 step).  A 4-stage ring with the DMA three chunks ahead and the next chunk's fragments read into
+// registers during the current chunk's MFMAs; one barrier per chunk.  Rows past M / N are clamped
+// to the last one (never stored).
+namespace {
+constexpr int kMxTile = 256;
+constexpr int kMxCodes = 8 * 2 * 1024;   // one operand's codes per stage
+constexpr int kMxScales = 8 * 256;       // one operand's scales per stage
+constexpr int kMxStage = 2 * (kMxCodes + kMxScales);
+constexpr int kMxStages = 4;
+constexpr int kMxSlots = 12;             // DMA loads per wave per chunk
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i as_v8(const u32x4 &v) {
+  const v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  return r;
+}
+
+// One 32x32x64 block-scaled FP4 MFMA of step T: op_sel 2T picks scale byte 2T of each lane's word.
+template <int T>
+__device__ __forceinline__ f32x16 mx_mfma(const u32x4 &row_op, const u32x4 &col_op, const f32x16 &c, uint32_t s_row,
+                                          uint32_t s_col) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8(row_op), as_v8(col_op), c, 4, 4, 2 * T, (int)s_row,
+                                                         2 * T, (int)s_col);
+}
+}  // namespace
+
+template <int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_mx_gemm(
+    const uint8_t *__restrict__ a, const uint8_t *__restrict__ as, const uint8_t *__restrict__ b,
+    const uint8_t *__restrict__ bs, int M, int N, int K, void *__restrict__ c, int64_t ldc, int tiles_m,
+    int tiles_n) {
+  constexpr int TM = 4, TN = 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // XCD-aware tile order (bijective on the multiple-of-8 prefix), as in the NVFP4 GEMM
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  {
+    const int full = (ntiles / 8) * 8;
+    if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+  }
+  const int m0 = (bid / tiles_n) * kMxTile, n0 = (bid % tiles_n) * kMxTile;
+  const int nk = K / 128;
+  const uint32_t rowb = (uint32_t)(K / 2), srow = (uint32_t)(K / 32);  // bytes per codes / scales row
+
+  // DMA sources: wave-uniform tile bases + 32-bit lane offsets (host: 256 * rowb < 2^31)
+  const uint8_t *a_tile = a + (int64_t)m0 * rowb, *as_tile = as + (int64_t)m0 * srow;
+  const uint8_t *b_tile = b + (int64_t)n0 * rowb, *bs_tile = bs + (int64_t)n0 * srow;
+  uint32_t oa[4], ob[4], oas[2], obs[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave + 4 * i, grp = q >> 1, st = q & 1;
+    const int ra = min(m0 + 32 * grp + lr, M - 1) - m0, rb = min(n0 + 32 * grp + lr, N - 1) - n0;
+    oa[i] = (uint32_t)ra * rowb + 32 * st + 16 * lh;
+    ob[i] = (uint32_t)rb * rowb + 32 * st + 16 * lh;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int grp = wave + 4 * i;
+    oas[i] = (uint32_t)(min(m0 + 32 * grp + lr, M - 1) - m0) * srow;
+    obs[i] = (uint32_t)(min(n0 + 32 * grp + lr, N - 1) - n0) * srow;
+  }
+  auto issue = [&](int kc, int stage) {
+    uint8_t *st = smem + stage * kMxStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g2l16(a_tile + (int64_t)kc * 64 + oa[i], st + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) g2l4(as_tile + kc * 4 + oas[i], st + kMxCodes + (wave + 4 * i) * 256);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      g2l16(b_tile + (int64_t)kc * 64 + ob[i], st + kMxCodes + kMxScales + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      g2l4(bs_tile + kc * 4 + obs[i], st + 2 * kMxCodes + kMxScales + (wave + 4 * i) * 256);
+  };
+
+  u32x4 Af[2][TM][2], Bf[2][TN][2];
+  uint32_t Sa[2][TM], Sb[2][TN];
+  auto read_frags = [&](int stage, int buf) {
+    const uint8_t *st = smem + stage * kMxStage;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int grp = wm * TM + i;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) Af[buf][i][t] = *reinterpret_cast<const u32x4 *>(st + (grp * 2 + t) * 1024 + lane * 16);
+      Sa[buf][i] = *reinterpret_cast<const uint32_t *>(st + kMxCodes + grp * 256 + lane * 4) >> (8 * lh);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int grp = wn * TN + j;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        Bf[buf][j][t] = *reinterpret_cast<const u32x4 *>(st + kMxCodes + kMxScales + (grp * 2 + t) * 1024 + lane * 16);
+      Sb[buf][j] = *reinterpret_cast<const uint32_t *>(st + 2 * kMxCodes + kMxScales + grp * 256 + lane * 4) >> (8 * lh);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Branch-free pipeline: near the end of K the DMA re-fetches the last chunk into the free stage
+  // and the look-ahead reads a stale stage; neither result is used.
+  issue(0, 0);
+  issue(min(1, nk - 1), 1);
+  issue(min(2, nk - 1), 2);
+  wait_vmem_then_barrier<2 * kMxSlots>();  // chunk 0 landed (chunks 1 and 2 may be in flight)
+  read_frags(0, 0);
+  // one chunk; CUR (compile time) is the register buffer holding its fragments
+  auto chunk = [&](int kc, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    wait_vmem_then_barrier<kMxSlots>();    // chunk kc+1 landed everywhere (kc+2 may be in flight)
+    issue(min(kc + 3, nk - 1), (kc + 3) % kMxStages);  // into the stage chunk kc-1 used
+    read_frags((kc + 1) % kMxStages, CUR ^ 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mx_mfma<0>(Bf[CUR][j][0], Af[CUR][i][0], acc[i][j], Sb[CUR][j], Sa[CUR][i]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mx_mfma<1>(Bf[CUR][j][1], Af[CUR][i][1], acc[i][j], Sb[CUR][j], Sa[CUR][i]);
+  };
+  int kc = 0;
+  for (; kc + 1 < nk; kc += 2) {
+    chunk(kc, std::integral_constant<int, 0>{});
+    chunk(kc + 1, std::integral_constant<int, 1>{});
+  }
+  if (kc < nk) chunk(kc, std::integral_constant<int, 0>{});
+
+  wait_vmem();      // the last look-ahead DMA targets the ring, which now stages output
+  __syncthreads();
+  typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
+  const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;
+  uint8_t *lds_wave = smem + wave * (32 * EpiPitch<128, 4>::kPitch);
+  store_tile<128, TM, TN, OutT>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec,
+                                lds_wave, lane);
+}
+
+// Generic fallback (any K % 32 == 0): one thread per output element.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_mx_gemm_generic(const uint8_t *__restrict__ a, const uint8_t *__restrict__ as,
+                                                         const uint8_t *__restrict__ b, const uint8_t *__restrict__ bs,
+                                                         int64_t M, int64_t N, int64_t K, void *__restrict__ c,
+                                                         int64_t ldc) {
+  for (int64_t t = blockIdx.x * 256ll + threadIdx.x; t < M * N; t += (int64_t)gridDim.x * 256) {
+    const int64_t m = t / N, n = t % N;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+      const uint32_t ca = (a[m * (K / 2) + k / 2] >> (4 * (k & 1))) & 15u;
+      const uint32_t cb = (b[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 15u;
+      const float xa = fp4_decode2_f32<0>(ca).x * mx_scale_value(as[m * (K / 32) + k / 32]);
+      const float xb = fp4_decode2_f32<0>(cb).x * mx_scale_value(bs[n * (K / 32) + k / 32]);
+      acc = fmaf(xa, xb, acc);
+    }
+    if (OUT == 0) static_cast<float *>(c)[m * ldc + n] = acc;
+    else static_cast<__bf16 *>(c)[m * ldc + n] = (__bf16)acc;
+  }
+}
+
+// ---- launchers --------------------------------------------------------------------------------------
+
+hipError_t launch_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+                              uint8_t *scales, hipStream_t stream) {
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / kMxBlk));
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
+  const int grid = mx_grid(nseg, kQuantizeMaxGrid);
+  const bool dense = (ld == K);
+  if (dtype == 0) {
+    if (dense) k_mx_quantize<0, true><<<grid, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales);
+    else k_mx_quantize<0, false><<<grid, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales);
+  } else {
+    if (dense) k_mx_quantize<1, true><<<grid, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales);
+    else k_mx_quantize<1, false><<<grid, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, void *y,
+                                int out_dtype, int64_t ld_y, hipStream_t stream) {
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / kMxBlk));
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (out_dtype == 0 ? 4u : 8u);
+  const int grid = mx_grid(nseg, kDequantizeMaxGrid);
+  const bool dense = (ld_y == K);
+  if (out_dtype == 0) {
+    if (dense) k_mx_dequantize<0, true><<<grid, 256, 0, stream>>>(packed, scales, nseg, bpr, y, ld_y);
+    else k_mx_dequantize<0, false><<<grid, 256, 0, stream>>>(packed, scales, nseg, bpr, y, ld_y);
+  } else {
+    if (dense) k_mx_dequantize<1, true><<<grid, 256, 0, stream>>>(packed, scales, nseg, bpr, y, ld_y);
+    else k_mx_dequantize<1, false><<<grid, 256, 0, stream>>>(packed, scales, nseg, bpr, y, ld_y);
+  }
+  return hipGetLastError();
+}
+
+template <int OUT>
+static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs,
+                                     int64_t M, int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
+  if (K % 128 != 0 || 256 * (K / 2) >= (int64_t(1) << 31)) {
+    int64_t grid = (M * N + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    k_mx_gemm_generic<OUT><<<(unsigned)grid, 256, 0, stream>>>(a, as, b, bs, M, N, K, c, ldc);
+    return hipGetLastError();
+  }
+  const int tm = (int)((M + kMxTile - 1) / kMxTile), tn = (int)((N + kMxTile - 1) / kMxTile);
+  constexpr int smem = kMxStages * kMxStage;
+  static_assert(4 * 32 * EpiPitch<128, 4>::kPitch <= smem, "epilogue staging fits the LDS ring");
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  k_mx_gemm<OUT><<<tm * tn, 256, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c, ldc, tm, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
+                          int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  return out_dtype == 0 ? launch_mx_gemm_out<0>(a, as, b, bs, M, N, K, c, ldc, stream)
+                        : launch_mx_gemm_out<1>(a, as, b, bs, M, N, K, c, ldc, stream);
+}
+
+}  // namespace nvfp4

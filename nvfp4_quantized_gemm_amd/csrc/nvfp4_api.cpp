@@ -221,4 +221,64 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
   return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+// ---- MXFP4 ------------------------------------------------------------------------------------
+
+namespace {
+nvfp4_status_t check_mx_mk(int64_t M, int64_t K) {
+  if (M < 0 || K < 32 || (K % 32) != 0) return NVFP4_ERR_SHAPE;
+  if (M > kMaxElems / K) return NVFP4_ERR_SHAPE;
+  if (M * (K / 16) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+}  // namespace
+
+nvfp4_status_t nvfp4_mx_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 uint8_t *packed, uint8_t *scales, void *stream) {
+  if (!valid_dtype(x_dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_mx_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (M == 0) return NVFP4_OK;
+  if (!x || !packed || !scales) return NVFP4_ERR_NULL;
+  if (ld_x < K) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || ((ld_x * elem_size(x_dtype)) % 16) != 0 || !aligned(packed, 8)) return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_mx_quantize(x, (int)x_dtype, M, K, ld_x, packed, scales, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_mx_dequantize(const uint8_t *packed, const uint8_t *scales, int64_t M, int64_t K, void *y,
+                                   nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
+  if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_mx_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (M == 0) return NVFP4_OK;
+  if (!packed || !scales || !y) return NVFP4_ERR_NULL;
+  if (ld_y < K) return NVFP4_ERR_STRIDE;
+  if (!aligned(y, 16) || ((ld_y * elem_size(y_dtype)) % 16) != 0 || !aligned(packed, 8)) return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_mx_dequantize(packed, scales, M, K, y, (int)y_dtype, ld_y, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_mx_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b, const uint8_t *b_scales,
+                             int64_t M, int64_t N, int64_t K, void *c, nvfp4_dtype_t c_dtype, int64_t ldc,
+                             void *stream) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_DTYPE;
+  if (N < 0) return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_mx_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  st = check_mx_mk(N, K);
+  if (st != NVFP4_OK) return st;
+  if (M >= (1 << 30) || N >= (1 << 30) || (N > 0 && M > kMaxElems / N)) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a || !a_scales || !b || !b_scales || !c) return NVFP4_ERR_NULL;
+  if (ldc < N) return NVFP4_ERR_STRIDE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) || !aligned(c, 16))
+    return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_mx_gemm(a, a_scales, b, b_scales, M, N, K, c, (int)c_dtype, ldc,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

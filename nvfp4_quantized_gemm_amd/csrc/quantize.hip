@@ -36,41 +36,6 @@
 
 namespace nvfp4 {
 
-// ---- input loading: one 16-byte segment per lane ------------------------------------------------
-
-template <int DT>
-struct SegIn;
-
-template <>
-struct SegIn<0> {  // fp32: 4 values
-  static constexpr int kElems = 4;
-  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem_off);
-  }
-  __device__ static void unpack(const u32x4 &w, float v[4]) {
-    v[0] = __uint_as_float(w.x);
-    v[1] = __uint_as_float(w.y);
-    v[2] = __uint_as_float(w.z);
-    v[3] = __uint_as_float(w.w);
-  }
-};
-
-template <>
-struct SegIn<1> {  // bf16: 8 values
-  static constexpr int kElems = 8;
-  __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem_off);
-  }
-  __device__ static void unpack(const u32x4 &w, float v[8]) {
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      v[2 * t] = bf16lo(a[t]);
-      v[2 * t + 1] = bf16hi(a[t]);
-    }
-  }
-};
-
 constexpr int kSegsPerLane = 4;  // segments in flight per lane
 
 // ---- exact pieces ---------------------------------------------------------------------------------
