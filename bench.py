@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at DiT shapes; % of MFMA/HBM roofline"
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (the block-scaled MXFP4 instruction)
 
 
 def parse():
@@ -37,6 +38,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
     ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernel section")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 section")
     ap.add_argument("--kernel-probe", action="store_true",
                     help="only launch the dominant GEMM call and a 256 MiB device copy, --steps times each "
                          "(the workload of the rocprofv3 counter passes)")
@@ -208,6 +210,8 @@ def main():
     }
     if not args.no_hbm:
         out["hbm_kernels"] = hbm_kernels(side, stream)
+    if not args.no_mx:
+        out["mxfp4"] = mxfp4_section(layers, side, stream, args.kernel_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
     print(json.dumps(out), flush=True)
@@ -352,6 +356,37 @@ def hbm_kernels(side, stream):
             res[f"w4a16_{name}_M{m}_N{N}_K{Kw}"] = e
         del bps
         torch.cuda.empty_cache()
+    return res
+
+
+def mxfp4_section(layers, side, stream, reps):
+    """The same block in MXFP4 (32-value E8M0 blocks, block-scaled FP4 matrix instruction): per
+    linear, the activation quantize and the GEMM (weights quantized beforehand), each timed as
+    back-to-back launches in one graph; the step is their sum."""
+    import torch
+
+    import nvfp4_quantized_gemm_amd as nv
+
+    res = {}
+    step_us = 0.0
+    flops_step = 0.0
+    for L in layers:
+        M, N, K = L["M"], L["N"], L["K"]
+        b, bs = nv.nvfp4_mx_quantize(L["w_cpu"].to(L["x"].device))
+        a = torch.empty((M, K // 2), dtype=torch.uint8, device=L["x"].device)
+        asc = torch.empty((M, K // 32), dtype=torch.uint8, device=L["x"].device)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=L["x"].device)
+        q_us = time_graph([lambda: nv.nvfp4_mx_quantize(L["x"], packed=a, scales=asc)] * reps, side, stream)
+        g_us = time_graph([lambda: nv.nvfp4_mx_gemm(a, asc, b, bs, out=y)] * reps, side, stream)
+        flops = 2.0 * M * N * K
+        tf = flops / (g_us * 1e-6) / 1e12
+        res[L["name"]] = {"quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2), "gemm_TFLOPs": round(tf, 1),
+                          "gemm_frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4)}
+        step_us += q_us + g_us
+        flops_step += flops
+    res["block_step_us"] = round(step_us, 2)
+    res["block_TFLOPs"] = round(flops_step / (step_us * 1e-6) / 1e12, 1)
+    res["peak_TFLOPs"] = PEAK_FP4_TFLOPS
     return res
 
 

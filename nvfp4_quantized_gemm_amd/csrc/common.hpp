@@ -99,6 +99,20 @@ __device__ __forceinline__ void wait_vmem_then_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Grouped raster over a tiles_m x tiles_n tile grid (bijective): consecutive indices walk down
+// groups of G tile rows before moving right, so a run of consecutive tiles (one XCD's share of a
+// round) touches about G row blocks of A and run / G column blocks of B instead of one row and
+// the whole width.
+template <int G>
+__device__ __forceinline__ void grouped_tile(int j, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int group_size = G * tiles_n;
+  const int group = j / group_size, r = j - group * group_size;
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
 // Lane swap across quads: lane i reads lane i ^ 4 (ds_swizzle bit mode, xor mask 4).
 __device__ __forceinline__ float swap_lane4(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));

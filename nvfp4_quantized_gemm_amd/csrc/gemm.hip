@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wm = wave / WN, wn = wave % WN;
 
   // XCD-aware tile order: consecutive dispatches land on different XCDs; give each XCD a
-  // contiguous range of tiles (row-major over the tile grid) so its L2 sees shared A rows.
+  // contiguous range of tiles in grouped-raster order (4 tile rows at a time) so its L2 sees
+  // shared A rows and shared B columns.
   // Split-K: workgroup = (tile, split); split s covers chunks [s Kc / splits, (s+1) Kc / splits).
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   const int split = bid / ntiles;
   bid -= split * ntiles;
-  const int tile_m = bid / tiles_n, tile_n = bid % tiles_n;
+  int tile_m, tile_n;
+  grouped_tile<4>(bid, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = m_off + tile_m * BM, n0 = n_off + tile_n * BN;
 
   const int Kc = K / kChunk;

@@ -215,14 +215,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // XCD-aware tile order (bijective on the multiple-of-8 prefix), as in the NVFP4 GEMM
+  // XCD-aware grouped tile order (bijective on the multiple-of-8 prefix), as in the NVFP4 GEMM
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   {
     const int full = (ntiles / 8) * 8;
     if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
   }
-  const int m0 = (bid / tiles_n) * kMxTile, n0 = (bid % tiles_n) * kMxTile;
+  int tmi, tni;
+  grouped_tile<4>(bid, tiles_m, tiles_n, tmi, tni);
+  const int m0 = tmi * kMxTile, n0 = tni * kMxTile;
   const int nk = K / 128;
   const uint32_t rowb = (uint32_t)(K / 2), srow = (uint32_t)(K / 32);  // bytes per codes / scales row
 
