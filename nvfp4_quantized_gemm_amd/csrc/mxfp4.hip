@@ -170,23 +170,28 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 
 // ---- GEMM: Y[M][N] = A[M][K] B[N][K]^T, both operands canonical MXFP4 ---------------------------------
 //
-// 256x256 tile per 256-thread workgroup (2 x 2 waves of 128 x 128 = 4 x 4 tiles of 32 x 32), K in
-// chunks of 128 (two 64-k MFMA steps).  LDS stage (36 KB):
-//   A codes  [8 row groups][2 steps][64 lanes][16 B]   A scales [8 row groups][64 lanes][4 B]
-//   B codes, B scales likewise (column groups).
-// Lane (r, h) of a codes block holds row 32 grp + r, bytes 32 step + 16 h of the chunk (k-half h of
-// the step); lane l of a scales block holds its row's 4 scale bytes of the chunk (block 2 step + h of
-// them is the one it feeds to the MFMA: the lane shifts the word right by 8 h and op_sel picks byte
-// 2 step).  A 4-stage ring with the DMA three chunks ahead and the next chunk's fragments read into
-// registers during the current chunk's MFMAs; one barrier per chunk.  Rows past M / N are clamped
-// to the last one (never stored).
+// 256 x 256 tile per workgroup of WM x WN waves, each owning (256 / WM) x (256 / WN) = TM x TN
+// tiles of 32 x 32: 2 x 2 waves (one per SIMD, 128 x 128 each) or 2 x 4 waves (two per SIMD,
+// 128 x 64 each, so one wave's LDS and DMA waits overlap the other's MFMAs).  K in chunks of 128
+// (two 64-k MFMA steps).  LDS stage (36 KB):
+//   A codes  [16 blocks of 16 rows][4 pieces][16 rows][16 B]   A scales [8 row groups][64 lanes][4 B]
+//   B codes, B scales likewise (columns).
+// A codes block holds 16 rows x the chunk's 64 bytes each, piece-major, so one DMA reads whole
+// 64-byte row segments and every 16-lane LDS read pass is contiguous; MFMA lane (r, h) of step s
+// reads piece 2 s + h of row r (k-half h of the step).  A scales word holds its row's 4 scale bytes
+// of the chunk (block 2 s + h of them feeds the MFMA: the lane shifts the word right by 8 h and
+// op_sel picks byte 2 s).  A 4-stage ring with
+// the DMA three chunks ahead and the next chunk's fragments read into registers during the current
+// chunk's MFMAs; one barrier per chunk.  Rows past M / N are clamped to the last one (never stored).
+#ifndef MX_WM
+#define MX_WM 2
+#endif
+#ifndef MX_WN
+#define MX_WN 4
+#endif
+
 namespace {
-constexpr int kMxTile = 256;
-constexpr int kMxCodes = 8 * 2 * 1024;   // one operand's codes per stage
-constexpr int kMxScales = 8 * 256;       // one operand's scales per stage
-constexpr int kMxStage = 2 * (kMxCodes + kMxScales);
-constexpr int kMxStages = 4;
-constexpr int kMxSlots = 12;             // DMA loads per wave per chunk
+constexpr int kMxTileM = 256;
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v8i as_v8(const u32x4 &v) {
@@ -201,18 +206,41 @@ __device__ __forceinline__ f32x16 mx_mfma(const u32x4 &row_op, const u32x4 &col_
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8(row_op), as_v8(col_op), c, 4, 4, 2 * T, (int)s_row,
                                                          2 * T, (int)s_col);
 }
+
+// LDS byte offset of lane (r, h)'s 16-byte operand of step t in row group grp: row r's piece
+// 2 t + h sits in codes block 2 grp + r / 16 at slot 16 (2 t + h) + r % 16, so a 16-lane read pass
+// is one contiguous 256-byte span (conflict-free).
+__device__ __forceinline__ int frag_off(int grp, int t, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  return (2 * grp + (r >> 4)) * 1024 + (16 * (2 * t + h) + (r & 15)) * 16;
+}
+
+template <int WM, int WN>
+struct MxCfg {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kTM = 8 / WM, kTN = 8 / WN;  // 32 x 32 tiles per wave
+  static constexpr int kCodes = 8 * 2 * 1024, kScales = 8 * 256;
+  static constexpr int kStage = 2 * (kCodes + kScales);
+  static constexpr int kStages = 4;
+  // DMA loads per wave per chunk, by kind (codes: 16 per operand, scales: 8 per operand)
+  static constexpr int kNC = 16 / kWaves, kNS = 8 / kWaves;
+  static constexpr int kSlots = 2 * (kNC + kNS);
+  static_assert(kNC * kWaves == 16 && kNS * kWaves == 8, "even DMA split");
+  static_assert(kStages * kStage <= 160 * 1024, "LDS ring fits");
+};
 }  // namespace
 
-template <int OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_mx_gemm(
+template <int OUT, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void k_mx_gemm(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ as, const uint8_t *__restrict__ b,
     const uint8_t *__restrict__ bs, int M, int N, int K, void *__restrict__ c, int64_t ldc, int tiles_m,
     int tiles_n) {
-  constexpr int TM = 4, TN = 4;
+  using Cfg = MxCfg<WM, WN>;
+  constexpr int TM = Cfg::kTM, TN = Cfg::kTN, S = Cfg::kStages, W = Cfg::kWaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
   // XCD-aware grouped tile order (bijective on the multiple-of-8 prefix), as in the NVFP4 GEMM
@@ -224,59 +252,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   int tmi, tni;
   grouped_tile<4>(bid, tiles_m, tiles_n, tmi, tni);
-  const int m0 = tmi * kMxTile, n0 = tni * kMxTile;
+  const int m0 = tmi * kMxTileM, n0 = tni * kMxTileM;
   const int nk = K / 128;
   const uint32_t rowb = (uint32_t)(K / 2), srow = (uint32_t)(K / 32);  // bytes per codes / scales row
 
   // DMA sources: wave-uniform tile bases + 32-bit lane offsets (host: 256 * rowb < 2^31)
   const uint8_t *a_tile = a + (int64_t)m0 * rowb, *as_tile = as + (int64_t)m0 * srow;
   const uint8_t *b_tile = b + (int64_t)n0 * rowb, *bs_tile = bs + (int64_t)n0 * srow;
-  uint32_t oa[4], ob[4], oas[2], obs[2];
+  uint32_t oa[Cfg::kNC], ob[Cfg::kNC], oas[Cfg::kNS], obs[Cfg::kNS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave + 4 * i, grp = q >> 1, st = q & 1;
-    const int ra = min(m0 + 32 * grp + lr, M - 1) - m0, rb = min(n0 + 32 * grp + lr, N - 1) - n0;
-    oa[i] = (uint32_t)ra * rowb + 32 * st + 16 * lh;
-    ob[i] = (uint32_t)rb * rowb + 32 * st + 16 * lh;
+  for (int i = 0; i < Cfg::kNC; ++i) {
+    // codes block d covers rows 16 d .. 16 d + 15 with all 64 bytes of each: lane l takes row
+    // 16 d + l % 16, 16-byte piece l / 16 (so a DMA touches 16 rows x 64 B, not 32 rows x 32 B)
+    const int d = wave + W * i, row16 = 16 * d + (lane & 15), piece = lane >> 4;
+    oa[i] = (uint32_t)(min(m0 + row16, M - 1) - m0) * rowb + 16 * piece;
+    ob[i] = (uint32_t)(min(n0 + row16, N - 1) - n0) * rowb + 16 * piece;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int grp = wave + 4 * i;
+  for (int i = 0; i < Cfg::kNS; ++i) {
+    const int grp = wave + W * i;
     oas[i] = (uint32_t)(min(m0 + 32 * grp + lr, M - 1) - m0) * srow;
     obs[i] = (uint32_t)(min(n0 + 32 * grp + lr, N - 1) - n0) * srow;
   }
   auto issue = [&](int kc, int stage) {
-    uint8_t *st = smem + stage * kMxStage;
+    uint8_t *st = smem + stage * Cfg::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g2l16(a_tile + (int64_t)kc * 64 + oa[i], st + (wave + 4 * i) * 1024);
+    for (int i = 0; i < Cfg::kNC; ++i) g2l16(a_tile + (int64_t)kc * 64 + oa[i], st + (wave + W * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) g2l4(as_tile + kc * 4 + oas[i], st + kMxCodes + (wave + 4 * i) * 256);
+    for (int i = 0; i < Cfg::kNS; ++i) g2l4(as_tile + kc * 4 + oas[i], st + Cfg::kCodes + (wave + W * i) * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      g2l16(b_tile + (int64_t)kc * 64 + ob[i], st + kMxCodes + kMxScales + (wave + 4 * i) * 1024);
+    for (int i = 0; i < Cfg::kNC; ++i)
+      g2l16(b_tile + (int64_t)kc * 64 + ob[i], st + Cfg::kCodes + Cfg::kScales + (wave + W * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      g2l4(bs_tile + kc * 4 + obs[i], st + 2 * kMxCodes + kMxScales + (wave + 4 * i) * 256);
+    for (int i = 0; i < Cfg::kNS; ++i)
+      g2l4(bs_tile + kc * 4 + obs[i], st + 2 * Cfg::kCodes + Cfg::kScales + (wave + W * i) * 256);
   };
 
   u32x4 Af[2][TM][2], Bf[2][TN][2];
   uint32_t Sa[2][TM], Sb[2][TN];
   auto read_frags = [&](int stage, int buf) {
-    const uint8_t *st = smem + stage * kMxStage;
+    const uint8_t *st = smem + stage * Cfg::kStage;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int grp = wm * TM + i;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) Af[buf][i][t] = *reinterpret_cast<const u32x4 *>(st + (grp * 2 + t) * 1024 + lane * 16);
-      Sa[buf][i] = *reinterpret_cast<const uint32_t *>(st + kMxCodes + grp * 256 + lane * 4) >> (8 * lh);
+      for (int t = 0; t < 2; ++t) Af[buf][i][t] = *reinterpret_cast<const u32x4 *>(st + frag_off(grp, t, lane));
+      Sa[buf][i] = *reinterpret_cast<const uint32_t *>(st + Cfg::kCodes + grp * 256 + lane * 4);
     }
+    const uint8_t *sb = st + Cfg::kCodes + Cfg::kScales;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int grp = wn * TN + j;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        Bf[buf][j][t] = *reinterpret_cast<const u32x4 *>(st + kMxCodes + kMxScales + (grp * 2 + t) * 1024 + lane * 16);
-      Sb[buf][j] = *reinterpret_cast<const uint32_t *>(st + 2 * kMxCodes + kMxScales + grp * 256 + lane * 4) >> (8 * lh);
+      for (int t = 0; t < 2; ++t) Bf[buf][j][t] = *reinterpret_cast<const u32x4 *>(sb + frag_off(grp, t, lane));
+      Sb[buf][j] = *reinterpret_cast<const uint32_t *>(sb + Cfg::kCodes + grp * 256 + lane * 4);
     }
   };
 
@@ -290,17 +319,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Branch-free pipeline: near the end of K the DMA re-fetches the last chunk into the free stage
   // and the look-ahead reads a stale stage; neither result is used.
-  issue(0, 0);
-  issue(min(1, nk - 1), 1);
-  issue(min(2, nk - 1), 2);
-  wait_vmem_then_barrier<2 * kMxSlots>();  // chunk 0 landed (chunks 1 and 2 may be in flight)
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(min(s, nk - 1), s);
+  wait_vmem_then_barrier<(S - 2) * Cfg::kSlots>();  // chunk 0 landed (later ones may be in flight)
   read_frags(0, 0);
   // one chunk; CUR (compile time) is the register buffer holding its fragments
   auto chunk = [&](int kc, auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
-    wait_vmem_then_barrier<kMxSlots>();    // chunk kc+1 landed everywhere (kc+2 may be in flight)
-    issue(min(kc + 3, nk - 1), (kc + 3) % kMxStages);  // into the stage chunk kc-1 used
-    read_frags((kc + 1) % kMxStages, CUR ^ 1);
+    wait_vmem_then_barrier<(S - 3) * Cfg::kSlots>();  // chunk kc+1 landed everywhere
+    // this chunk's scale words (read one chunk ago): lane (r, h) feeds blocks h and 2 + h, i.e.
+    // bytes 0 and 2 after a shift by 8 h.  Done before the next reads are issued, so waiting for
+    // the old reads does not wait for the new ones.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) Sa[CUR][i] >>= 8 * lh;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) Sb[CUR][j] >>= 8 * lh;
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(kc + S - 1, nk - 1), (kc + S - 1) % S);   // into the stage chunk kc-1 used
+    read_frags((kc + 1) % S, CUR ^ 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -321,9 +357,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __syncthreads();
   typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
   const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;
-  uint8_t *lds_wave = smem + wave * (32 * EpiPitch<128, 4>::kPitch);
-  store_tile<128, TM, TN, OutT>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec,
-                                lds_wave, lane);
+  constexpr int CW = 256 / WN;  // columns per wave
+  static_assert(W * 32 * EpiPitch<CW, 4>::kPitch <= S * Cfg::kStage, "epilogue staging fits the LDS ring");
+  uint8_t *lds_wave = smem + wave * (32 * EpiPitch<CW, 4>::kPitch);
+  store_tile<CW, TM, TN, OutT>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * (256 / WM), n0 + wn * CW,
+                               vec, lds_wave, lane);
 }
 
 // Generic fallback (any K % 32 == 0): one thread per output element.
@@ -381,6 +419,24 @@ hipError_t launch_mx_dequantize(const uint8_t *packed, const uint8_t *scales, in
   return hipGetLastError();
 }
 
+template <int OUT, int WM, int WN>
+static hipError_t launch_mx_tiled(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
+                                  int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
+  using Cfg = MxCfg<WM, WN>;
+  const int tm = (int)((M + kMxTileM - 1) / kMxTileM), tn = (int)((N + kMxTileM - 1) / kMxTileM);
+  constexpr int smem = Cfg::kStages * Cfg::kStage;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, WM, WN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  k_mx_gemm<OUT, WM, WN><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c, ldc, tm,
+                                                                     tn);
+  return hipGetLastError();
+}
+
 template <int OUT>
 static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs,
                                      int64_t M, int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
@@ -390,18 +446,7 @@ static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const 
     k_mx_gemm_generic<OUT><<<(unsigned)grid, 256, 0, stream>>>(a, as, b, bs, M, N, K, c, ldc);
     return hipGetLastError();
   }
-  const int tm = (int)((M + kMxTile - 1) / kMxTile), tn = (int)((N + kMxTile - 1) / kMxTile);
-  constexpr int smem = kMxStages * kMxStage;
-  static_assert(4 * 32 * EpiPitch<128, 4>::kPitch <= smem, "epilogue staging fits the LDS ring");
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
-  k_mx_gemm<OUT><<<tm * tn, 256, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c, ldc, tm, tn);
-  return hipGetLastError();
+  return launch_mx_tiled<OUT, MX_WM, MX_WN>(a, as, b, bs, M, N, K, c, ldc, stream);
 }
 
 hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
