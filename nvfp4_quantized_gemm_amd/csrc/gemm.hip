@@ -42,10 +42,10 @@ struct TileCfg {
   static constexpr int kBSChunks = BN / 2;                                          // 16-B chunks of B scales
 };
 
-__device__ __forceinline__ f16x8 dequant_f16x8(uint32_t codes, _Float16 e) {
-  const f16x2 ee = {e, e};
-  const f16x2 q[4] = {fp4_decode2_f16<0>(codes) * ee, fp4_decode2_f16<1>(codes) * ee,
-                      fp4_decode2_f16<2>(codes) * ee, fp4_decode2_f16<3>(codes) * ee};
+// exact E2M1 decode of the 8 codes of a dword (element 2j in the low nibble of byte j)
+__device__ __forceinline__ f16x8 decode_f16x8(uint32_t codes) {
+  const f16x2 q[4] = {fp4_decode2_f16<0>(codes), fp4_decode2_f16<1>(codes), fp4_decode2_f16<2>(codes),
+                      fp4_decode2_f16<3>(codes)};
   f16x8 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -53,6 +53,11 @@ __device__ __forceinline__ f16x8 dequant_f16x8(uint32_t codes, _Float16 e) {
     r[2 * j + 1] = q[j].y;
   }
   return r;
+}
+
+__device__ __forceinline__ f16x8 scale_f16x8(const f16x8 &q, _Float16 e) {
+  const f16x8 ee = {e, e, e, e, e, e, e, e};
+  return q * ee;  // q * e is exact in fp16
 }
 
 __device__ __forceinline__ bf16x8 dequant_bf16x8(uint32_t codes, float e) {
@@ -195,15 +200,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (kend <= kbeg) {
     // empty K range (not produced by the planner): leave the accumulators at zero
   } else if (MODE == 0) {
-    // ---- W4A4: one continuous stream of 16-k steps.  Step s+1 is dequantized while step s's 16
-    // MFMAs run (also across chunk boundaries).  Codes are held per half-chunk ("part", 4 steps):
+    // ---- W4A4: one continuous stream of 16-k steps.  Dequantization is a two-stage pipeline that
+    // runs beside step s's 16 MFMAs (also across chunk boundaries): the codes of step s+2 are
+    // decoded to exact E2M1 values (Q registers) and the decoded values of step s+1 are multiplied
+    // by their block scales (F registers), so no VALU result is consumed by the next instruction
+    // and the VALU work co-issues with the MFMAs.  Codes are held per half-chunk ("part", 4 steps):
     // part 1 of chunk kc is read at the start of chunk kc, part 0 of chunk kc+1 (and its scales) at
     // step 3, so every LDS read has >= 3 steps of MFMA work to land.  A 3-stage LDS ring with the
     // DMA two chunks ahead leaves one barrier per chunk.
     u32x4 P0a[TM], P0b[TN], P1a[TM], P1b[TN];
     uint32_t Sa[TM], Sb[TN];
     f16x2 Ea[TM][2], Eb[TN][2], Na[TM][2], Nb[TN][2];
-    f16x8 Fa[2][TM], Fb[2][TN];
+    f16x8 Fa[2][TM], Fb[2][TN], Qa[2][TM], Qb[2][TN];
 
     auto stage = [&](int buf) { return smem + buf * Cfg::kStage; };
     auto read_part = [&](u32x4 *ra, u32x4 *rb, int buf, int part) {
@@ -244,13 +252,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         eb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[j], 1.0f, true);
       }
     };
-    // dequantize step s (0..7) of a chunk from part registers (ra, rb) with scales (ea, eb)
-    auto deq = [&](const u32x4 *ra, const u32x4 *rb, f16x2 (*ea)[2], f16x2 (*eb)[2], int s, int slot) {
-      const int q = s & 3, blk = s >> 1;
+    // stage 1: decode the codes of step s (0..7) of a chunk from part registers (ra, rb) into Q[s & 1]
+    auto cvt_step = [&](const u32x4 *ra, const u32x4 *rb, int s) {
+      const int q = s & 3, slot = s & 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) Fa[slot][i] = dequant_f16x8(ra[i][q], ea[i][blk >> 1][blk & 1]);
+      for (int i = 0; i < TM; ++i) Qa[slot][i] = decode_f16x8(ra[i][q]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) Fb[slot][j] = dequant_f16x8(rb[j][q], eb[j][blk >> 1][blk & 1]);
+      for (int j = 0; j < TN; ++j) Qb[slot][j] = decode_f16x8(rb[j][q]);
+    };
+    // stage 2: F[s & 1] = Q[s & 1] * block scale of step s, with scales (ea, eb) of its chunk
+    auto mul_step = [&](f16x2 (*ea)[2], f16x2 (*eb)[2], int s) {
+      const int blk = s >> 1, slot = s & 1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) Fa[slot][i] = scale_f16x8(Qa[slot][i], ea[i][blk >> 1][blk & 1]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Fb[slot][j] = scale_f16x8(Qb[slot][j], eb[j][blk >> 1][blk & 1]);
     };
     auto mfma_step = [&](int slot) {
 #pragma unroll
@@ -282,7 +298,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     read_part(P0a, P0b, 0, 0);
     read_scales(0);
     cvt_scales(Ea, Eb);
-    deq(P0a, P0b, Ea, Eb, 0, 0);
+    cvt_step(P0a, P0b, 0);
+    cvt_step(P0a, P0b, 1);
+    mul_step(Ea, Eb, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // One chunk of 8 steps.  FIRST (compile time) is the peeled first chunk: it has no top wait
@@ -314,13 +332,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int u = 0; u < kPer; ++u)
           if (s * kPer + u < NSLOT) issue_slot(kdma, bdma, s * kPer + u);
         if (s == 3) {
-          read_part(P0a, P0b, bnext, 0);  // P0 of this chunk was last used by step 3's dequant
+          read_part(P0a, P0b, bnext, 0);  // P0 of this chunk was last decoded in step 1
           read_scales(bnext);
         }
         if (s == 6) cvt_scales(Na, Nb);
-        if (s < 3) deq(P0a, P0b, Ea, Eb, s + 1, slot ^ 1);
-        else if (s < 7) deq(P1a, P1b, Ea, Eb, s + 1, slot ^ 1);
-        else deq(P0a, P0b, Na, Nb, 0, slot ^ 1);
+        // stage 2 for step s+1, stage 1 for step s+2 (steps 8 and 9 are the next chunk's 0 and 1)
+        if (s < 7) mul_step(Ea, Eb, s + 1);
+        else mul_step(Na, Nb, 0);
+        if (s < 2) cvt_step(P0a, P0b, s + 2);
+        else if (s < 6) cvt_step(P1a, P1b, s + 2);
+        else cvt_step(P0a, P0b, s - 6);
         mfma_step(slot);
         interleave();
         if (s < 6) __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);  // this step's DMA loads
