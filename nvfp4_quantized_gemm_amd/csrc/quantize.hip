@@ -27,9 +27,14 @@
 //  * Element codes.  inv = rcp(e) * RN32(1/S) is within 3 ulp of 1/(e S); lo = RN32(inv (1 - 2^-20))
 //    and hi = RN32(inv (1 + 2^-20)) make the fp32 products v*lo and v*hi bracket v/(e S) strictly.
 //    The hardware E2M1 conversion (round-half-even, saturating, sign-preserving) is monotone, so
-//    when the two bracketing codes agree that code is the exact one.  A block in which any pair
-//    disagrees (a value within ~2^-19 of a decision boundary, e.g. an exact tie) takes the exact
-//    path: seven per-block fp32 thresholds U_k from the exact fp64 boundaries t_k e S by directed
+//    when the two bracketing codes agree that code is the exact one.  When they disagree (a value
+//    within ~2^-19 of a decision boundary, e.g. an exact tie) the bracket holds exactly one
+//    boundary, between the two adjacent candidate codes, and one exact fp64 comparison of |v|
+//    with that boundary t e S (<= 3 + 4 + 24 significant bits, exact) picks the code, ties to the
+//    even one.  The block scale byte is settled the same way between its two candidate bytes.
+//    (Scales whose mantissa is a ratio of small integers, e.g. 1.1 * 2^k, make such near-ties
+//    common, so this path must be cheap.)  Outside the bracket's range of S a full exact path
+//    runs: seven per-block fp32 thresholds U_k from the exact fp64 boundaries by directed
 //    rounding, code = #{k : |v| >= U_k}.
 #include "common.hpp"
 #include "launch.hpp"
@@ -132,6 +137,24 @@ __device__ __forceinline__ uint32_t encode_values(const float *v, uint32_t byte,
       const uint32_t m = pick * 15u;                  // widen to whole nibbles (no carries)
       return (lo & ~m) | (hi & m);
     }
+    // A differing nibble has adjacent magnitudes m (lo) and m + 1 (hi) and the same sign: the
+    // bracket is ~2^-19 wide and consecutive boundaries are >= 40 % apart.  Decide |v| against
+    // the boundary t_m e S between them, exactly in fp64.
+    const double es = (double)e * (double)S;  // exact: 4 + 24 significant bits
+    uint32_t out = lo;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t a = (lo >> (4 * i)) & 15u, b = (hi >> (4 * i)) & 15u;
+      if (a != b) {
+        const uint32_t m = a & 7u;
+        const double t = (m < 4u) ? 0.25 + 0.5 * (double)m : (m == 4u ? 2.5 : (m == 5u ? 3.5 : 5.0));
+        const double bound = t * es;  // exact: <= 3 + 4 + 24 significant bits
+        const double x = fabs((double)v[i]);
+        const uint32_t mag = (x > bound) ? m + 1u : (x < bound ? m : ((m & 1u) ? m + 1u : m));
+        out = (out & ~(15u << (4 * i))) | (((a & 8u) | mag) << (4 * i));
+      }
+    }
+    return out;
   }
   return codes_exact<N>(v, e, S);
 }
@@ -142,7 +165,16 @@ __device__ __forceinline__ uint32_t block_byte(float amax, float S, float rlo, f
   if (fast_ok) {
     const float ra = fminf(amax * rlo, kE4M3Max), rb = fminf(amax * rhi, kE4M3Max);
     const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
-    if ((pk & 0xffu) == ((pk >> 8) & 0xffu)) return pk & 0xffu;
+    const uint32_t b0 = pk & 0xffu, b1 = (pk >> 8) & 0xffu;
+    if (b0 == b1) return b0;
+    if (b1 == b0 + 1u) {
+      // the ratio amax / (6 S) lies within ~2^-19 of the midpoint of two adjacent E4M3 values:
+      // compare amax with 6 * midpoint * S, exact in fp64 (<= 8 + 24 significant bits)
+      const double mid = 0.5 * ((double)e4m3_to_f32(b0) + (double)e4m3_to_f32(b1));
+      const double bound = 6.0 * mid * (double)S;
+      const double a = (double)amax;
+      return (a > bound) ? b1 : (a < bound ? b0 : ((b0 & 1u) ? b1 : b0));
+    }
   }
   return scale_byte_exact(amax, S);
 }

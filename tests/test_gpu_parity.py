@@ -134,6 +134,24 @@ def test_quantize_extreme_static_scales():
     assert_quantize_exact(x, static_S=2.0 ** 110, label="huge S")
 
 
+@pytest.mark.parametrize("S", [1.1 * 2.0 ** -9, 1.5 * 2.0 ** -9, 1.25 * 2.0 ** -9, 1.75 * 2.0 ** -10,
+                               2.0 ** -8 / 3.0, 2.0 ** -9 / 7.0, 1.0 / 2688.0])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_quantize_near_tie_scales(S, dt):
+    """Static scales whose mantissa is a ratio of small integers put many values (and block maxima)
+    exactly on, or within an fp32 rounding of, a decision boundary t e S or an E4M3 midpoint; every
+    such value is decided by the exact two-candidate comparison.  Inputs: random values plus
+    dyadic multiples of the block scale (on-boundary candidates)."""
+    g = torch.Generator().manual_seed(int(S * 2.0 ** 40) % 100003)
+    M, K = 512, 2048
+    x = torch.randn(M, K, generator=g) * 0.5
+    # every third row: small integers times 2^-k, so t e S boundaries are hit exactly or nearly
+    ints = torch.randint(-48, 49, (M // 3, K), generator=g).to(torch.float32)
+    x[::3][: M // 3] = ints * 2.0 ** -7
+    x = x.to(dt)
+    assert_quantize_exact(x, static_S=float(np.float32(S)), label=f"near-tie S={S:.6g}")
+
+
 def test_quantize_sweep_full_size_largest():
     """Largest sweep tensor (32768 x 12288 bf16, 403M values), dynamic, full comparison."""
     x = workloads.sweep(32768, 12288)
