@@ -333,6 +333,16 @@ def hbm_kernels(side, stream):
     us = time_graph([lambda: nv.nvfp4_fake_quantize(x, S, static=False, out=yq, workspace=qws)] * reps, side, stream)
     res[f"fake_quantize_dynamic_bf16_{M}x{K}"] = entry(us, n * (2 + 2 + 2))
     del yq
+    # The sweep's planted 10.5 makes the dynamic S exactly 2^-8, which keeps every decision on the
+    # cheap exact-tie path.  A plain N(0, 1) tensor of the same size gives a generic S.
+    g = torch.Generator().manual_seed(41)
+    x.copy_(torch.randn(M, K, generator=g).to(torch.bfloat16))
+    us = time_graph([lambda: nv.nvfp4_quantize(x, S, static=False, packed=packed, scales=scales, workspace=qws)] * reps,
+                    side, stream)
+    res[f"quantize_dynamic_bf16_{M}x{K}_generic_S"] = entry(us, n * (2 + 2 + 0.5625))
+    res[f"quantize_dynamic_bf16_{M}x{K}_generic_S"]["S"] = float(S.item())
+    us = time_graph([lambda: nv.nvfp4_quantize(x, S, static=True, packed=packed, scales=scales)] * reps, side, stream)
+    res[f"quantize_static_bf16_{M}x{K}_generic_S"] = entry(us, n * (2 + 0.5625))
     del x, packed, scales, y
     torch.cuda.empty_cache()
 

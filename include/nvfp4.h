@@ -169,6 +169,39 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
                           size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * GEMM with NVFP4 output (epilogue-fused requantization) [NVFP4-DiT page, Methodology section 3:
+ * packed operands for the next W4A4 product, produced on the fly; Definition III.1 for the
+ * encoding].  The product is formed exactly as in nvfp4_gemm; in fp32,
+ *     y = acc * S_A * S_B  (+ bias[n] when bias != NULL)  (then act(y))
+ * and y is quantized under the STATIC output tensor scale *out_tensor_scale with nvfp4_quantize's
+ * rules (exact decisions on the fp32 value y), written in the canonical layout: out_packed
+ * [M][N/2] bytes, out_scales [M][N/16] E4M3 bytes.  The result can feed nvfp4_gemm as the next
+ * W4A4 activation (lda = N) together with out_tensor_scale.  A dynamic output scale would need the
+ * whole output's maximum before the first block is encoded, so it is not offered.
+ *
+ *   mode, a, a_scales, a_tensor_scale, b_prepacked, b_tensor_scale, M, N, K, lda: as nvfp4_gemm.
+ *   N % 16 == 0 (the output's 16-value blocks run along N).
+ *   bias           NULL or device fp32 [N], 16-byte aligned.
+ *   act            NVFP4_ACT_NONE, or NVFP4_ACT_GELU_TANH: 0.5 y (1 + tanh(sqrt(2/pi)(y + 0.044715 y^3)))
+ *                  (the pages do not name the MLP activation; the tanh form of GELU is the one of
+ *                  the DiT-family MLPs they build on).
+ *   out_tensor_scale  device fp32 static S of the output (finite, > 0).
+ *   out_packed     device [M][N/2], 16-byte aligned.   out_scales  device [M][N/16].
+ *   y              NULL, or device fp32 [M][ld_y] (ld_y >= N, ld_y % 4 == 0, 16-byte aligned) that
+ *                  also receives the fp32 values that were quantized.
+ *   workspace      nvfp4_gemm_requant_workspace_bytes(mode, M, N, K) bytes, 16-byte aligned.
+ *   M == 0 or N == 0 is valid and touches nothing.
+ * ------------------------------------------------------------------------------------------- */
+typedef enum { NVFP4_ACT_NONE = 0, NVFP4_ACT_GELU_TANH = 1 } nvfp4_act_t;
+
+size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
+nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                                  const float *a_tensor_scale, const void *b_prepacked, const float *b_tensor_scale,
+                                  int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,
+                                  const float *out_tensor_scale, uint8_t *out_packed, uint8_t *out_scales, float *y,
+                                  int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * MXFP4, the related microscaling format (vllm-omni RFC, Motivation; the pages do not define it,
  * the OCP microscaling definition is followed): blocks of 32 consecutive values along K share one
  * E8M0 scale byte b (X = 2^(b - 127)), X = 2^(floor(log2 amax) - 2) with b clamped to [0, 254] and

@@ -40,6 +40,7 @@ EXPORTED = (
     "nvfp4_dequantize", "nvfp4_fake_quantize",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_gemm_requant_workspace_bytes", "nvfp4_gemm_requant",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
 )
 
@@ -84,6 +85,11 @@ def lib():
     L.nvfp4_gemm_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
     L.nvfp4_gemm.restype = _i
     L.nvfp4_gemm.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _i64, _vp, _sz, _vp]
+    L.nvfp4_gemm_requant_workspace_bytes.restype = _sz
+    L.nvfp4_gemm_requant_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
+    L.nvfp4_gemm_requant.restype = _i
+    L.nvfp4_gemm_requant.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _vp, _vp, _vp,
+                                     _vp, _i64, _vp, _sz, _vp]
     L.nvfp4_mx_quantize.restype = _i
     L.nvfp4_mx_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _vp, _vp]
     L.nvfp4_mx_dequantize.restype = _i
@@ -280,6 +286,42 @@ def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked
     return out
 
 
+ACT_NONE, ACT_GELU_TANH = 0, 1
+
+
+def nvfp4_gemm_requant_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_requant_workspace_bytes(mode, M, N, K))
+
+
+def nvfp4_gemm_requant(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked: torch.Tensor,
+                       b_tensor_scale: torch.Tensor, N: int, K: int, out_tensor_scale: torch.Tensor, *,
+                       bias=None, act: int = ACT_NONE, packed=None, scales=None, y=None, workspace=None,
+                       stream=None):
+    """NVFP4 output of A B^T (+ bias) (-> act) under the static out_tensor_scale (device fp32 [1]).
+    Operands as nvfp4_gemm.  Returns (packed u8 [M, N/2], scales u8 [M, N/16]); when y (fp32 [M, >= N])
+    is given it also receives the fp32 values that were quantized."""
+    M = a.shape[0]
+    if mode == W4A4:
+        lda = a.stride(0) * 2
+    else:
+        _, _, lda = _rows(a, "a")
+    if packed is None:
+        packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty((M, N // 16), dtype=torch.uint8, device=a.device)
+    ldy = 0 if y is None else y.stride(0)
+    ws_need = nvfp4_gemm_requant_workspace_bytes(mode, M, N, K)
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_gemm_requant(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_prepacked),
+                                  _ptr(b_tensor_scale), M, N, K, lda, _ptr(bias), act, _ptr(out_tensor_scale),
+                                  _ptr(packed), _ptr(scales), _ptr(y), ldy, _ptr(workspace), ws_bytes,
+                                  _stream(stream))
+    _check(st, "nvfp4_gemm_requant")
+    return packed, scales
+
+
 # ---- MXFP4 (32-value blocks, E8M0 scales, no tensor scale) ------------------------------------
 
 def nvfp4_mx_quantize(x: torch.Tensor, *, packed=None, scales=None, stream=None):
@@ -324,5 +366,6 @@ __all__ = [
     "FakeQuantizeSTE", "fake_quantize_ste",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+    "ACT_NONE", "ACT_GELU_TANH", "nvfp4_gemm_requant_workspace_bytes", "nvfp4_gemm_requant",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
 ]

@@ -1,6 +1,8 @@
 // Output epilogue shared by the tiled GEMM kernels (gfx950).
 #pragma once
 #include "common.hpp"
+#include "launch.hpp"
+#include "quant_core.hpp"
 
 namespace nvfp4 {
 
@@ -74,6 +76,96 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
           }
         }
       }
+    }
+    wave_lds_sync();  // the next slab overwrites this region
+  }
+}
+
+// ---- NVFP4 output (epilogue-fused requantization) ------------------------------------------------
+//
+// The GEMM result y = acc * S_A * S_B (+ bias[n]) (-> activation) is computed in fp32 and written
+// as NVFP4 under the caller's static tensor scale, with the quantizer's exact rounding rules
+// [NVFP4-DiT page, Methodology section 3 (packed operands produced for the next W4A4 product) and
+// Definition III.1].  A lane holds 4 consecutive columns of one row; the four lanes 4k .. 4k+3 of
+// a quad hold one 16-column block (the output N is a multiple of 16, so a quad is wholly inside
+// or wholly outside the matrix).
+
+__device__ __forceinline__ float apply_act(float v, int act) {
+  if (act == kActGeluTanh) {
+    // GELU, tanh form: 0.5 v (1 + tanh(sqrt(2 / pi) (v + 0.044715 v^3)))
+    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+    return 0.5f * v * (1.0f + tanhf(u));
+  }
+  return v;
+}
+
+// Quantize and store one lane's 4 values (columns col .. col+3 of `row`).  Every lane of the quad
+// must call this (the block maximum is exchanged across the quad); `valid` is uniform per quad.
+__device__ __forceinline__ void requant4(f32x4 acc, int64_t row, int64_t col, bool valid, int64_t N,
+                                         const QuantOut &qo, const QuantConsts &qc, int lane) {
+  float v[4] = {acc.x, acc.y, acc.z, acc.w};
+  if (qo.bias && valid) {
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(qo.bias + col);
+    v[0] += b.x;
+    v[1] += b.y;
+    v[2] += b.z;
+    v[3] += b.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = apply_act(v[i], qo.act);
+  if (qo.y && valid) {
+    const f32x4 o = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(qo.y + row * qo.ldy + col) = o;
+  }
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  amax = fmaxf(amax, swap_lane1(amax));
+  amax = fmaxf(amax, swap_lane2(amax));
+  if (!valid) return;
+  const uint32_t byte = block_byte(amax, qc);
+  uint32_t codes = 0;
+  if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
+#pragma unroll
+    for (int i = 0; i < 4; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+  } else {
+    codes = encode_values<4>(v, byte, qc);
+  }
+  *reinterpret_cast<uint16_t *>(qo.packed + row * (N / 2) + col / 2) = (uint16_t)codes;
+  if ((lane & 3) == 0) qo.scales[row * (N / 16) + col / 16] = (uint8_t)byte;
+}
+
+// store_tile for NVFP4 output: the wave's sub-tile goes through the same padded row-major fp32
+// staging as store_tile, and each read-back vector (4 consecutive columns) is requantized.
+template <int CW, int TM, int TN>
+__device__ __forceinline__ void store_tile_nvfp4(const f32x16 (&acc)[TM][TN], float scale, const QuantOut &qo,
+                                                 int M, int N, int row0, int col0, uint8_t *lds, int lane) {
+  constexpr int kPitch = EpiPitch<CW, 4>::kPitch;
+  constexpr int kLanesPerRow = CW / 4;
+  constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  static_assert(CW == 32 * TN && kLanesPerRow <= 64 && 64 % kLanesPerRow == 0 && kLanesPerRow % 4 == 0,
+                "epilogue shape");
+  const QuantConsts qc = make_quant_consts(*qo.out_ts, false);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rr = lane / kLanesPerRow, cq = (lane % kLanesPerRow) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 o = {__float_as_uint(acc[i][j][4 * g] * scale), __float_as_uint(acc[i][j][4 * g + 1] * scale),
+                         __float_as_uint(acc[i][j][4 * g + 2] * scale), __float_as_uint(acc[i][j][4 * g + 3] * scale)};
+        *reinterpret_cast<u32x4 *>(lds + lr * kPitch + (j * 32 + 8 * g + 4 * lh) * 4) = o;
+      }
+    }
+    wave_lds_sync();
+    // not unrolled: the requantization is long, and a short slab body lets the slab loop unroll, so
+    // the accumulators are only ever indexed at compile time (no copy in scratch memory)
+#pragma unroll 1
+    for (int t = 0; t < 32 / kRowsPerRead; ++t) {
+      const int r = t * kRowsPerRead + rr;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(lds + r * kPitch + cq * 4);
+      const int row = row0 + i * 32 + r, col = col0 + cq;
+      requant4(v, row, col, row < M && col < N, N, qo, qc, lane);
     }
     wave_lds_sync();  // the next slab overwrites this region
   }

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
     void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int m_off, int n_off, int splits,
-    float *__restrict__ partial) {
+    float *__restrict__ partial, QuantOut qo) {
   using Cfg = TileCfg<MODE, BM, BN>;
   constexpr int TM = BM / WM / 32;  // MFMA tiles per wave along M
   constexpr int TN = BN / WN / 32;
@@ -434,9 +434,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return;
   }
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
-  typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
-  const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;  // 16-byte aligned rows
-  store_tile<BN / WN, TM, TN, OutT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec, lds_wave, lane);
+  if constexpr (OUT == 2) {
+    store_tile_nvfp4<BN / WN, TM, TN>(acc, sab, qo, M, N, row0, col0, lds_wave, lane);
+  } else {
+    typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
+    const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;  // 16-byte aligned rows
+    store_tile<BN / WN, TM, TN, OutT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec, lds_wave,
+                                      lane);
+  }
 }
 
 // ---- generic fallback (any K % 16 == 0): one thread per output element ---------------------------
@@ -483,21 +488,27 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const void *__restrict__ a
 }
 
 // ---- split-K reduction: C = (sum over splits, in order) * S_A S_B, deterministic ----------------
+// OUT 2 writes NVFP4 (QuantOut): a lane holds 4 consecutive outputs, so the lanes of a quad hold one
+// 16-column block (N % 16 == 0; the quads of a wave leave the loop together).
 
 template <int OUT>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial, int splits, int M, int N,
                                                        void *__restrict__ c, int64_t ldc, const float *__restrict__ a_ts,
-                                                       const float *__restrict__ b_ts) {
-  const float sab = a_ts ? (*a_ts) * (*b_ts) : *b_ts;
+                                                       const float *__restrict__ b_ts, QuantOut qo) {
+  const float sab = (a_ts ? *a_ts : 1.0f) * (b_ts ? *b_ts : 1.0f);
   const int64_t MN = (int64_t)M * N;
   const bool vec = (ldc % 4 == 0);  // 4-element stores stay aligned (c is 16-byte aligned)
   const int64_t nq = MN / 4;  // N % 4 == 0 here
+  QuantConsts qc;
+  if (OUT == 2) qc = make_quant_consts(*qo.out_ts, false);
   for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < nq; q += (int64_t)gridDim.x * 256) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + 4 * q);
     for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4 *>(partial + sp * MN + 4 * q);
     const int64_t m = (4 * q) / N, n = (4 * q) % N;
     acc *= sab;
-    if (OUT == 0) {
+    if (OUT == 2) {
+      requant4(acc, m, n, true, N, qo, qc, threadIdx.x & 63);
+    } else if (OUT == 0) {
       float *dst = static_cast<float *>(c) + m * ldc + n;
       if (vec) {
         *reinterpret_cast<f32x4 *>(dst) = acc;
@@ -526,14 +537,17 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 }
 
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
-                                int64_t ldc, const float *a_ts, const float *b_ts, hipStream_t stream) {
+                                int64_t ldc, const float *a_ts, const float *b_ts, const QuantOut &qo,
+                                hipStream_t stream) {
   int64_t grid = (M * N / 4 + 255) / 256;
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
   if (out_dtype == 0)
-    k_splitk_reduce<0><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts);
+    k_splitk_reduce<0><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts, qo);
+  else if (out_dtype == 1)
+    k_splitk_reduce<1><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts, qo);
   else
-    k_splitk_reduce<1><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts);
+    k_splitk_reduce<2><<<(unsigned)grid, 256, 0, stream>>>(partial, splits, (int)M, (int)N, c, ldc, a_ts, b_ts, qo);
   return hipGetLastError();
 }
 
@@ -555,7 +569,7 @@ static hipError_t launch_tiled(const GemmArgs &g, int m_off, int n_off, int m_le
   }
   kern<<<tm * tn * splits, 256, smem, stream>>>(g.a, g.a_scales, g.a_ts, static_cast<const uint8_t *>(g.b), g.b_ts,
                                                 (int)g.M, (int)g.N, (int)g.K, g.lda, g.c, g.ldc, tm, tn, m_off, n_off,
-                                                splits, partial);
+                                                splits, partial, g.qo);
   return hipGetLastError();
 }
 
@@ -630,6 +644,14 @@ size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
   return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
+  const GemmPlan pl = plan_gemm(mode, M, N, K, K);
+  const size_t mn = (size_t)M * (size_t)N * sizeof(float);
+  // the generic and skinny kernels produce fp32 first; the reduction pass requantizes
+  if (pl.variant == GemmVariant::Generic || pl.variant == GemmVariant::W4A16_Skinny) return (size_t)pl.splits * mn;
+  return pl.splits > 1 ? (size_t)pl.splits * mn : 0;
+}
+
 template <int OUT>
 static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t stream) {
   const int M = (int)g.M, N = (int)g.N;
@@ -639,7 +661,7 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         float *part = static_cast<float *>(g.workspace);
         hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
         if (e != hipSuccess) return e;
-        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, stream);
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, g.qo, stream);
       }
       if (pl.n_big > 0 && pl.n_big < N) {
         hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, (int)pl.n_big, 1, nullptr, stream);
@@ -655,7 +677,7 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         float *part = static_cast<float *>(g.workspace);
         hipError_t e = launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
         if (e != hipSuccess) return e;
-        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, stream);
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
       }
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
     }
@@ -669,6 +691,21 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
   const GemmPlan pl = plan_gemm(g.mode, g.M, g.N, g.K, g.lda);
+  if (g.out_dtype == 2) {
+    // NVFP4 output: the tile kernels requantize in their epilogue (or in the split-K reduction);
+    // the generic kernel writes scaled fp32 into the workspace and the reduction pass requantizes
+    if (pl.variant == GemmVariant::Generic) {
+      GemmArgs f = g;
+      f.c = g.workspace;
+      f.ldc = g.N;
+      f.out_dtype = 0;
+      hipError_t e = g.mode == 0 ? launch_generic<0, 0>(f, stream) : launch_generic<1, 0>(f, stream);
+      if (e != hipSuccess) return e;
+      return launch_splitk_reduce(static_cast<const float *>(g.workspace), 1, g.M, g.N, nullptr, 2, 0, nullptr,
+                                  nullptr, g.qo, stream);
+    }
+    return run_plan<2>(g, pl, stream);
+  }
   if (pl.variant == GemmVariant::Generic) {
     if (g.mode == 0) return g.out_dtype == 0 ? launch_generic<0, 0>(g, stream) : launch_generic<0, 1>(g, stream);
     return g.out_dtype == 0 ? launch_generic<1, 0>(g, stream) : launch_generic<1, 1>(g, stream);

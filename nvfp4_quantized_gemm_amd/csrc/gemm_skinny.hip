@@ -135,8 +135,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
   if (!has_row) return;
   const int n = 32 * u + 8 * wave + 4 * h;
-  if (splits > 1) {
+  if (OUT == 2 || splits > 1) {
     // unscaled fp32 partial; the split-K reduction sums the splits in order, scales and converts
+    // (OUT 2, NVFP4 output: always, the reduction pass requantizes)
     float *dst = partial + (int64_t)split * M * N + (int64_t)r * N + n;
     if (n + 3 < N && (N % 4) == 0) {
       const f32x4 o = {out[0], out[1], out[2], out[3]};
@@ -191,10 +192,11 @@ static hipError_t launch_skinny_out(const GemmArgs &g, int nw, int splits, float
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *partial, hipStream_t stream) {
-  hipError_t e = g.out_dtype == 0 ? launch_skinny_out<0>(g, waves, splits, partial, stream)
-                                  : launch_skinny_out<1>(g, waves, splits, partial, stream);
-  if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(partial, splits, g.M, g.N, g.c, g.out_dtype, g.ldc, nullptr, g.b_ts, stream);
+  hipError_t e = g.out_dtype == 0   ? launch_skinny_out<0>(g, waves, splits, partial, stream)
+                 : g.out_dtype == 1 ? launch_skinny_out<1>(g, waves, splits, partial, stream)
+                                    : launch_skinny_out<2>(g, waves, splits, partial, stream);
+  if (e != hipSuccess || (splits == 1 && g.out_dtype != 2)) return e;
+  return launch_splitk_reduce(partial, splits, g.M, g.N, g.c, g.out_dtype, g.ldc, nullptr, g.b_ts, g.qo, stream);
 }
 
 }  // namespace nvfp4

@@ -32,6 +32,20 @@ struct GemmPlan {
   int64_t n_big = 0;  // > 0: columns [0, n_big) in 256x256 tiles, the rest in 128x128 tiles
 };
 
+// NVFP4 output of the GEMM (epilogue-fused requantization): y = acc S_A S_B (+ bias) (-> act),
+// quantized under the static tensor scale *out_ts into canonical packed [M][N/2] / scales [M][N/16];
+// optionally also written as fp32 to y [M][ldy].
+constexpr int kActNone = 0, kActGeluTanh = 1;
+struct QuantOut {
+  const float *bias = nullptr;    // [N] fp32 or null
+  const float *out_ts = nullptr;  // device fp32 static tensor scale of the output
+  uint8_t *packed = nullptr;
+  uint8_t *scales = nullptr;
+  float *y = nullptr;
+  int64_t ldy = 0;
+  int act = kActNone;
+};
+
 struct GemmArgs {
   int mode;  // 0 W4A4, 1 W4A16
   const void *a;
@@ -41,23 +55,27 @@ struct GemmArgs {
   const float *b_ts;
   int64_t M, N, K, lda;
   void *c;
-  int out_dtype;  // 0 f32, 1 bf16
+  int out_dtype;  // 0 f32, 1 bf16, 2 NVFP4 (qo)
   int64_t ldc;
   void *workspace;
+  QuantOut qo;
 };
 
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+// workspace of the NVFP4-output GEMM: fp32 partials wherever the plan does not end in a tile kernel
+size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 
 // W4A16 with M <= kSkinnyMaxM: streaming kernel over the prepacked weight (gemm_skinny.hip)
 constexpr int kSkinnyMaxM = 32;
 hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *partial, hipStream_t stream);
 
-// C = (sum of the splits' fp32 partials [splits][M][N], in order) * (a_ts ? *a_ts : 1) * *b_ts;
-// needs N % 4 == 0
+// C = (sum of the splits' fp32 partials [splits][M][N], in order) * (a_ts ? *a_ts : 1) *
+// (b_ts ? *b_ts : 1); needs N % 4 == 0 (N % 16 == 0 for out_dtype 2, which writes qo)
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
-                                int64_t ldc, const float *a_ts, const float *b_ts, hipStream_t stream);
+                                int64_t ldc, const float *a_ts, const float *b_ts, const QuantOut &qo,
+                                hipStream_t stream);
 
 // MXFP4 (mxfp4.hip): 32-value blocks with E8M0 scales, GEMM on the block-scaled FP4 MFMA.
 hipError_t launch_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,

@@ -221,6 +221,73 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
   return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+// ---- GEMM with NVFP4 output ------------------------------------------------------------------
+
+size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+  if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return 0;
+  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || (N % 16) != 0) return 0;  // empty or invalid calls
+  return gemm_requant_workspace_bytes((int)mode, M, N, K);
+}
+
+nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                                  const float *a_tensor_scale, const void *b_prepacked, const float *b_tensor_scale,
+                                  int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,
+                                  const float *out_tensor_scale, uint8_t *out_packed, uint8_t *out_scales, float *y,
+                                  int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream) {
+  if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return NVFP4_ERR_MODE;
+  if (mode == NVFP4_W4A16 && (a_scales || a_tensor_scale)) return NVFP4_ERR_NULL;
+  if (act != NVFP4_ACT_NONE && act != NVFP4_ACT_GELU_TANH) return NVFP4_ERR_MODE;
+  if (N < 0 || (N % 16) != 0) return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;  // empty output: nothing to read or write
+  if (!a || !b_prepacked || !b_tensor_scale || !out_tensor_scale || !out_packed || !out_scales)
+    return NVFP4_ERR_NULL;
+  if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
+  if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
+  if (lda < K) return NVFP4_ERR_STRIDE;
+  if (y && (ld_y < N || (ld_y % 4) != 0)) return NVFP4_ERR_STRIDE;
+  if (mode == NVFP4_W4A4) {
+    if ((lda % 16) != 0) return NVFP4_ERR_STRIDE;
+    if (!aligned(a, 8)) return NVFP4_ERR_ALIGN;
+  } else {
+    if (!aligned(a, 16) || ((lda * 2) % 16) != 0) return NVFP4_ERR_ALIGN;
+  }
+  if (!aligned(b_prepacked, 16) || !aligned(b_tensor_scale, 4) || !aligned(out_tensor_scale, 4) ||
+      !aligned(out_packed, 16) || (bias && !aligned(bias, 16)) || (y && !aligned(y, 16)))
+    return NVFP4_ERR_ALIGN;
+  const size_t need = nvfp4_gemm_requant_workspace_bytes(mode, M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  GemmArgs g;
+  g.mode = (int)mode;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.a_ts = a_tensor_scale;
+  g.b = b_prepacked;
+  g.b_ts = b_tensor_scale;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.c = nullptr;
+  g.out_dtype = 2;
+  g.ldc = 0;
+  g.workspace = workspace;
+  g.qo.bias = bias;
+  g.qo.out_ts = out_tensor_scale;
+  g.qo.packed = out_packed;
+  g.qo.scales = out_scales;
+  g.qo.y = y;
+  g.qo.ldy = ld_y;
+  g.qo.act = (int)act;
+  return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
 // ---- MXFP4 ------------------------------------------------------------------------------------
 
 namespace {

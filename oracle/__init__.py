@@ -229,3 +229,27 @@ def gemm_sampled(A: np.ndarray, B: np.ndarray, rows, cols):
 def bf16_to_f32(x16: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float32 (no arithmetic of the method)."""
     return (x16.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- linear-layer epilogue before requantization ------------------------------------------------
+# The GEMM with NVFP4 output forms y = Y (+ bias[n]) (-> activation) and quantizes y under a static
+# tensor scale with the rules of `quantize` [NVFP4-DiT page, Methodology section 3: operands of the
+# next W4A4 product; Definition III.1: the encoding].  The pages name no activation; the tanh form
+# of GELU (the DiT-family MLP activation) is the reading taken.
+
+def gelu_tanh(x) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x * x * x)))
+
+
+def linear_epilogue(Y: np.ndarray, bias=None, act: int = 0) -> np.ndarray:
+    """y = Y + bias (per output column, fp64) followed by the activation (0: none, 1: GELU tanh)."""
+    y = np.asarray(Y, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if act == 1:
+        y = gelu_tanh(y)
+    elif act != 0:
+        raise ValueError("unknown activation")
+    return y

@@ -138,6 +138,41 @@ def test_gemm_validation(L):
     assert g(L, mode=nv.W4A16, asc=NULL, ats=NULL, a=P8) == S.ERR_ALIGN
 
 
+def rq(L, mode=nv.W4A4, a=P, asc=P, ats=P, b=P, bts=P, M=64, N=64, K=128, lda=128, bias=NULL, act=0, ots=P,
+       op=P, osc=P, y=NULL, ldy=0, ws=NULL, wsb=0):
+    return L.nvfp4_gemm_requant(mode, a, asc, ats, b, bts, M, N, K, lda, bias, act, ots, op, osc, y, ldy, ws, wsb,
+                                None)
+
+
+def test_gemm_requant_validation(L):
+    S = nv.Status
+    assert rq(L, mode=9) == S.ERR_MODE
+    assert rq(L, act=7) == S.ERR_MODE
+    assert rq(L, N=40) == S.ERR_SHAPE              # output blocks run along N: N % 16 == 0
+    assert rq(L, N=-16) == S.ERR_SHAPE
+    assert rq(L, K=100, lda=112) == S.ERR_SHAPE
+    assert rq(L, ots=NULL) == S.ERR_NULL
+    assert rq(L, op=NULL) == S.ERR_NULL
+    assert rq(L, osc=NULL) == S.ERR_NULL
+    assert rq(L, mode=nv.W4A16) == S.ERR_NULL      # W4A16 must not pass A scales
+    assert rq(L, lda=64) == S.ERR_STRIDE
+    assert rq(L, y=P, ldy=32) == S.ERR_STRIDE       # ld_y >= N
+    assert rq(L, y=P, ldy=66) == S.ERR_STRIDE       # ld_y % 4 == 0
+    assert rq(L, bias=P8) == S.ERR_ALIGN
+    assert rq(L, op=P8) == S.ERR_ALIGN
+    assert rq(L, y=P8, ldy=64) == S.ERR_ALIGN
+    # a split-K shape needs the fp32 partials; so does the generic kernel (K % 128 != 0)
+    need = L.nvfp4_gemm_requant_workspace_bytes(nv.W4A4, 512, 512, 4096)
+    assert need >= 4 * 512 * 512 * 2
+    assert rq(L, M=512, N=512, K=4096, lda=4096) == S.ERR_WORKSPACE
+    assert rq(L, M=512, N=512, K=4096, lda=4096, ws=P, wsb=need - 1) == S.ERR_WORKSPACE
+    assert L.nvfp4_gemm_requant_workspace_bytes(nv.W4A4, 64, 96, 48) == 64 * 96 * 4
+    assert L.nvfp4_gemm_requant_workspace_bytes(nv.W4A4, 64, 40, 128) == 0   # invalid N
+    # empty outputs touch nothing
+    assert rq(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, ots=NULL, op=NULL, osc=NULL, M=0) == S.OK
+    assert rq(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, ots=NULL, op=NULL, osc=NULL, N=0) == S.OK
+
+
 def test_empty_tensors_touch_nothing(L):
     """M == 0 (or N == 0 for the GEMM and the weight calls) is valid: the call returns OK at once,
     before any device work, with NULL pointers for the empty arrays.  (Dynamic quantization of an

@@ -538,3 +538,32 @@ def test_bf16_input_equals_fp32_of_same_values():
     assert S1 == S2
     np.testing.assert_array_equal(p1, p2)
     np.testing.assert_array_equal(s1, s2)
+
+
+# ---- linear epilogue (GELU, bias) of the NVFP4-output GEMM ---------------------------------------
+
+def test_gelu_tanh_matches_torch_and_identities():
+    """Pinned by torch's own tanh-form GELU in fp64 (library routine) and by two closed forms:
+    g(x) - g(-x) = x exactly for this form (the tanh terms cancel), and g(0) = 0."""
+    g = torch.Generator().manual_seed(17)
+    x = torch.cat([torch.randn(4096, generator=g, dtype=torch.float64) * 4,
+                   torch.tensor([0.0, -0.0, 1e-300, -1e-300, 3.0, -3.0, 40.0, -40.0], dtype=torch.float64)])
+    ours = oracle.gelu_tanh(x.numpy())
+    ref = torch.nn.functional.gelu(x, approximate="tanh").numpy()
+    # for large negative x both forms lose relative accuracy to the cancellation in 1 + tanh(u),
+    # so the bound is relative to |g| plus a few ulps of |x|
+    xa = np.abs(x.numpy())
+    assert np.all(np.abs(ours - ref) <= 1e-14 * np.abs(ref) + 4e-16 * xa)
+    assert np.all(np.abs((ours - oracle.gelu_tanh(-x.numpy())) - x.numpy()) <= 4e-16 * xa)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_tanh(40.0) == 40.0 and abs(oracle.gelu_tanh(-40.0)) < 1e-300 + 1e-12
+
+
+def test_linear_epilogue_bias_per_column():
+    Y = np.arange(12, dtype=np.float64).reshape(3, 4)
+    b = np.array([1.0, -2.0, 0.5, 0.0])
+    np.testing.assert_array_equal(oracle.linear_epilogue(Y, b, 0), Y + b[None, :])
+    np.testing.assert_array_equal(oracle.linear_epilogue(Y, None, 0), Y)
+    np.testing.assert_allclose(oracle.linear_epilogue(Y, b, 1),
+                               torch.nn.functional.gelu(torch.from_numpy(Y + b[None, :]), approximate="tanh").numpy(),
+                               rtol=1e-14)
