@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
     ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernel section")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 section")
+    ap.add_argument("--no-requant", action="store_true", help="skip the fused-requantization section")
     ap.add_argument("--kernel-probe", action="store_true",
                     help="only launch the dominant GEMM call and a 256 MiB device copy, --steps times each "
                          "(the workload of the rocprofv3 counter passes)")
@@ -212,6 +213,8 @@ def main():
         out["hbm_kernels"] = hbm_kernels(side, stream)
     if not args.no_mx:
         out["mxfp4"] = mxfp4_section(layers, side, stream, args.kernel_reps)
+    if not args.no_requant:
+        out["fused_requant"] = requant_section(layers, side, stream, args.kernel_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
     print(json.dumps(out), flush=True)
@@ -397,6 +400,61 @@ def mxfp4_section(layers, side, stream, reps):
     res["block_step_us"] = round(step_us, 2)
     res["block_TFLOPs"] = round(flops_step / (step_us * 1e-6) / 1e12, 1)
     res["peak_TFLOPs"] = PEAK_FP4_TFLOPS
+    return res
+
+
+def requant_section(layers, side, stream, reps):
+    """The block's MLP pair (fc1 -> fc2) with the fc1 GEMM writing NVFP4 directly (tanh GELU, static
+    output scale calibrated on an eager run) against the unfused sequence the step uses (fc1 with
+    bf16 output, dynamic quantize of that output, fc2).  The unfused sequence does no GELU, so the
+    fused one does strictly more work.  Each piece is timed as back-to-back launches in one graph."""
+    import torch
+
+    import nvfp4_quantized_gemm_amd as nv
+
+    by = {L["name"]: L for L in layers}
+    f1, f2 = by["fc1"], by["fc2"]
+    dev = f1["x"].device
+    M, N1, K1 = f1["M"], f1["N"], f1["K"]
+    # fc1 activation (quantized as in the step) and the bf16 fc1 output of the unfused path
+    nv.nvfp4_quantize(f1["x"], f1["S"], static=False, packed=f1["packed"], scales=f1["scales"], workspace=f1["qws"])
+    h16 = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+    hp = torch.empty((M, N1 // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, N1 // 16), dtype=torch.uint8, device=dev)
+    hS = torch.empty(1, dtype=torch.float32, device=dev)
+    hws = torch.empty(nv.nvfp4_quantize_workspace_bytes(M, N1), dtype=torch.uint8, device=dev)
+    y2 = torch.empty((M, f2["N"]), dtype=torch.bfloat16, device=dev)
+    # calibration: the static scale of the GELU output, from one eager fp32 pass
+    hy = torch.empty((M, N1), dtype=torch.float32, device=dev)
+    cal = torch.ones(1, dtype=torch.float32, device=dev)
+    nv.nvfp4_gemm_requant(nv.W4A4, f1["packed"], f1["scales"], f1["S"], f1["bp"], f1["wS"], N1, K1, cal,
+                          act=nv.ACT_GELU_TANH, packed=hp, scales=hs, y=hy)
+    So = (hy.abs().max() / 2688.0).reshape(1).contiguous()
+    del hy
+    rws = nv.nvfp4_gemm_requant_workspace_bytes(nv.W4A4, M, N1, K1)
+    rws_t = torch.empty(max(rws, 1), dtype=torch.uint8, device=dev)
+
+    def fc1_bf16():
+        nv.nvfp4_gemm(nv.W4A4, f1["packed"], f1["scales"], f1["S"], f1["bp"], f1["wS"], N1, K1, torch.bfloat16,
+                      out=h16, workspace=f1["gws"])
+
+    def quant_dyn():
+        nv.nvfp4_quantize(h16, hS, static=False, packed=hp, scales=hs, workspace=hws)
+
+    def fc1_requant():
+        nv.nvfp4_gemm_requant(nv.W4A4, f1["packed"], f1["scales"], f1["S"], f1["bp"], f1["wS"], N1, K1, So,
+                              act=nv.ACT_GELU_TANH, packed=hp, scales=hs, workspace=rws_t)
+
+    def fc2_from_h(S):
+        nv.nvfp4_gemm(nv.W4A4, hp, hs, S, f2["bp"], f2["wS"], f2["N"], f2["K"], torch.bfloat16, out=y2,
+                      workspace=f2["gws"])
+
+    res = {"M": M, "fc1": [N1, K1], "fc2": [f2["N"], f2["K"]], "static_S": float(So.item())}
+    res["fc1_gemm_bf16_us"] = round(time_graph([fc1_bf16] * reps, side, stream), 2)
+    res["fc2_act_quantize_dynamic_us"] = round(time_graph([quant_dyn] * reps, side, stream), 2)
+    res["fc1_gemm_gelu_requant_us"] = round(time_graph([fc1_requant] * reps, side, stream), 2)
+    res["mlp_unfused_us"] = round(time_graph([fc1_bf16, quant_dyn, lambda: fc2_from_h(hS)] * 4, side, stream) * 3, 2)
+    res["mlp_fused_us"] = round(time_graph([fc1_requant, lambda: fc2_from_h(So)] * 4, side, stream) * 2, 2)
     return res
 
 

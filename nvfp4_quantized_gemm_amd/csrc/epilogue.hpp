@@ -86,66 +86,92 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
 // The GEMM result y = acc * S_A * S_B (+ bias[n]) (-> activation) is computed in fp32 and written
 // as NVFP4 under the caller's static tensor scale, with the quantizer's exact rounding rules
 // [NVFP4-DiT page, Methodology section 3 (packed operands produced for the next W4A4 product) and
-// Definition III.1].  A lane holds 4 consecutive columns of one row; the four lanes 4k .. 4k+3 of
-// a quad hold one 16-column block (the output N is a multiple of 16, so a quad is wholly inside
-// or wholly outside the matrix).
+// Definition III.1].  A lane owns one whole 16-column block of one row (the output N is a multiple
+// of 16, so a block is wholly inside or wholly outside the matrix).
 
 __device__ __forceinline__ float apply_act(float v, int act) {
   if (act == kActGeluTanh) {
-    // GELU, tanh form: 0.5 v (1 + tanh(sqrt(2 / pi) (v + 0.044715 v^3)))
-    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-    return 0.5f * v * (1.0f + tanhf(u));
+    // GELU, tanh form: 0.5 v (1 + tanh(u)), u = sqrt(2 / pi) (v + 0.044715 v^3).  Evaluated through
+    // the identity 0.5 (1 + tanh u) = 1 / (1 + exp(-2 u)) with the hardware exp2 and reciprocal
+    // (about 1 ulp each): no cancellation for negative v, and the limits come out exactly
+    // (exp -> inf gives v * 0 = -0, exp -> 0 gives v).  exp(-2 u) = 2^(v (c1 + c3 v^2)).
+    constexpr float c1 = -1.5957691216057308f * 1.4426950408889634f;
+    constexpr float c3 = c1 * 0.044715f;
+    const float t = __builtin_amdgcn_exp2f(v * (c1 + c3 * (v * v)));
+    return v * __builtin_amdgcn_rcpf(1.0f + t);
   }
   return v;
 }
 
-// Quantize and store one lane's 4 values (columns col .. col+3 of `row`).  Every lane of the quad
-// must call this (the block maximum is exchanged across the quad); `valid` is uniform per quad.
-__device__ __forceinline__ void requant4(f32x4 acc, int64_t row, int64_t col, bool valid, int64_t N,
-                                         const QuantOut &qo, const QuantConsts &qc, int lane) {
-  float v[4] = {acc.x, acc.y, acc.z, acc.w};
-  if (qo.bias && valid) {
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(qo.bias + col);
-    v[0] += b.x;
-    v[1] += b.y;
-    v[2] += b.z;
-    v[3] += b.w;
-  }
+// Requantize and store the 16 values v[0..15] = columns col .. col+15 of `row` (a whole block).
+// Branch-light: the common case is decided by the brackets; lanes whose bracket is ambiguous (rare)
+// are settled exactly behind one wave-uniform test.
+__device__ __forceinline__ void requant16(float (&v)[16], int64_t row, int64_t col, bool valid, int64_t N,
+                                          const QuantOut &qo, const QuantConsts &qc) {
+  if (qo.bias) {  // uniform; a lane outside the matrix reads column 0 (in bounds) and is not stored
+    const f32x4 *bp = reinterpret_cast<const f32x4 *>(qo.bias + (valid ? col : 0));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = apply_act(v[i], qo.act);
-  if (qo.y && valid) {
-    const f32x4 o = {v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(qo.y + row * qo.ldy + col) = o;
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 b = bp[h];
+      v[4 * h] += b.x;
+      v[4 * h + 1] += b.y;
+      v[4 * h + 2] += b.z;
+      v[4 * h + 3] += b.w;
+    }
   }
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  amax = fmaxf(amax, swap_lane1(amax));
-  amax = fmaxf(amax, swap_lane2(amax));
-  if (!valid) return;
-  const uint32_t byte = block_byte(amax, qc);
-  uint32_t codes = 0;
-  if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
+  if (qo.act == kActGeluTanh) {  // uniform
 #pragma unroll
-    for (int i = 0; i < 4; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
-  } else {
-    codes = encode_values<4>(v, byte, qc);
+    for (int i = 0; i < 16; ++i) v[i] = apply_act(v[i], kActGeluTanh);
   }
-  *reinterpret_cast<uint16_t *>(qo.packed + row * (N / 2) + col / 2) = (uint16_t)codes;
-  if ((lane & 3) == 0) qo.scales[row * (N / 16) + col / 16] = (uint8_t)byte;
+  if (qo.y) {  // uniform
+    if (valid) {
+      f32x4 *yp = reinterpret_cast<f32x4 *>(qo.y + row * qo.ldy + col);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 o = {v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+        yp[h] = o;
+      }
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  bool amb_b, amb_0, amb_1;
+  uint32_t byte = block_byte_fast(amax, qc, amb_b);
+  const float inv = __builtin_amdgcn_rcpf(e4m3_to_f32(byte)) * qc.invS;
+  const float ilo = byte ? inv * (1.0f - 0x1p-20f) : 0.0f, ihi = byte ? inv * (1.0f + 0x1p-20f) : 0.0f;
+  uint32_t c0 = encode8_bracket(v, ilo, ihi, amb_0);
+  uint32_t c1 = encode8_bracket(v + 8, ilo, ihi, amb_1);
+  const bool exact = valid && (amb_b || amb_0 || amb_1 || !qc.fast_ok);
+  if (__builtin_amdgcn_ballot_w64(exact) != 0) {  // rare
+    if (exact) {
+      byte = block_byte(amax, qc);
+      if (byte != 0) {
+        c0 = encode_values<8>(v, byte, qc);
+        c1 = encode_values<8>(v + 8, byte, qc);
+      }
+    }
+  }
+  if (valid) {
+    const u32x2 o = {c0, c1};
+    *reinterpret_cast<u32x2 *>(qo.packed + row * (N / 2) + col / 2) = o;
+    qo.scales[row * (N / 16) + col / 16] = (uint8_t)byte;
+  }
 }
 
 // store_tile for NVFP4 output: the wave's sub-tile goes through the same padded row-major fp32
-// staging as store_tile, and each read-back vector (4 consecutive columns) is requantized.
+// staging as store_tile; each lane then reads back one whole 16-column block of a row and
+// requantizes it.
 template <int CW, int TM, int TN>
 __device__ __forceinline__ void store_tile_nvfp4(const f32x16 (&acc)[TM][TN], float scale, const QuantOut &qo,
                                                  int M, int N, int row0, int col0, uint8_t *lds, int lane) {
   constexpr int kPitch = EpiPitch<CW, 4>::kPitch;
-  constexpr int kLanesPerRow = CW / 4;
+  constexpr int kLanesPerRow = CW / 16;
   constexpr int kRowsPerRead = 64 / kLanesPerRow;
-  static_assert(CW == 32 * TN && kLanesPerRow <= 64 && 64 % kLanesPerRow == 0 && kLanesPerRow % 4 == 0,
-                "epilogue shape");
+  static_assert(CW == 32 * TN && 64 % kLanesPerRow == 0 && 32 % kRowsPerRead == 0, "epilogue shape");
   const QuantConsts qc = make_quant_consts(*qo.out_ts, false);
   const int lr = lane & 31, lh = lane >> 5;
-  const int rr = lane / kLanesPerRow, cq = (lane % kLanesPerRow) * 4;
+  const int rr = lane / kLanesPerRow, cb = (lane % kLanesPerRow) * 16;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -158,14 +184,22 @@ __device__ __forceinline__ void store_tile_nvfp4(const f32x16 (&acc)[TM][TN], fl
       }
     }
     wave_lds_sync();
-    // not unrolled: the requantization is long, and a short slab body lets the slab loop unroll, so
-    // the accumulators are only ever indexed at compile time (no copy in scratch memory)
+    // not unrolled: a short slab body lets the slab loop unroll, so the accumulators are only ever
+    // indexed at compile time (no copy in scratch memory)
 #pragma unroll 1
     for (int t = 0; t < 32 / kRowsPerRead; ++t) {
       const int r = t * kRowsPerRead + rr;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(lds + r * kPitch + cq * 4);
-      const int row = row0 + i * 32 + r, col = col0 + cq;
-      requant4(v, row, col, row < M && col < N, N, qo, qc, lane);
+      float v[16];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 q = *reinterpret_cast<const f32x4 *>(lds + r * kPitch + (cb + 4 * h) * 4);
+        v[4 * h] = q.x;
+        v[4 * h + 1] = q.y;
+        v[4 * h + 2] = q.z;
+        v[4 * h + 3] = q.w;
+      }
+      const int row = row0 + i * 32 + r, col = col0 + cb;
+      requant16(v, row, col, row < M && col < N, N, qo, qc);
     }
     wave_lds_sync();  // the next slab overwrites this region
   }

@@ -488,8 +488,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const void *__restrict__ a
 }
 
 // ---- split-K reduction: C = (sum over splits, in order) * S_A S_B, deterministic ----------------
-// OUT 2 writes NVFP4 (QuantOut): a lane holds 4 consecutive outputs, so the lanes of a quad hold one
-// 16-column block (N % 16 == 0; the quads of a wave leave the loop together).
+// OUT 2 writes NVFP4 (QuantOut): a thread sums and requantizes one 16-value block.
 
 template <int OUT>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial, int splits, int M, int N,
@@ -497,18 +496,33 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
                                                        const float *__restrict__ b_ts, QuantOut qo) {
   const float sab = (a_ts ? *a_ts : 1.0f) * (b_ts ? *b_ts : 1.0f);
   const int64_t MN = (int64_t)M * N;
+  if constexpr (OUT == 2) {
+    // a thread owns one 16-value block (N % 16 == 0)
+    const QuantConsts qc = make_quant_consts(*qo.out_ts, false);
+    for (int64_t b = blockIdx.x * 256ll + threadIdx.x; b < MN / 16; b += (int64_t)gridDim.x * 256) {
+      float v[16];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        f32x4 a = *reinterpret_cast<const f32x4 *>(partial + 16 * b + 4 * h);
+        for (int sp = 1; sp < splits; ++sp) a += *reinterpret_cast<const f32x4 *>(partial + sp * MN + 16 * b + 4 * h);
+        a *= sab;
+        v[4 * h] = a.x;
+        v[4 * h + 1] = a.y;
+        v[4 * h + 2] = a.z;
+        v[4 * h + 3] = a.w;
+      }
+      requant16(v, (16 * b) / N, (16 * b) % N, true, N, qo, qc);
+    }
+    return;
+  }
   const bool vec = (ldc % 4 == 0);  // 4-element stores stay aligned (c is 16-byte aligned)
   const int64_t nq = MN / 4;  // N % 4 == 0 here
-  QuantConsts qc;
-  if (OUT == 2) qc = make_quant_consts(*qo.out_ts, false);
   for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < nq; q += (int64_t)gridDim.x * 256) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + 4 * q);
     for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4 *>(partial + sp * MN + 4 * q);
     const int64_t m = (4 * q) / N, n = (4 * q) % N;
     acc *= sab;
-    if (OUT == 2) {
-      requant4(acc, m, n, true, N, qo, qc, threadIdx.x & 63);
-    } else if (OUT == 0) {
+    if (OUT == 0) {
       float *dst = static_cast<float *>(c) + m * ldc + n;
       if (vec) {
         *reinterpret_cast<f32x4 *>(dst) = acc;
@@ -539,7 +553,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N, void *c, int out_dtype,
                                 int64_t ldc, const float *a_ts, const float *b_ts, const QuantOut &qo,
                                 hipStream_t stream) {
-  int64_t grid = (M * N / 4 + 255) / 256;
+  int64_t grid = (M * N / (out_dtype == 2 ? 16 : 4) + 255) / 256;
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
   if (out_dtype == 0)

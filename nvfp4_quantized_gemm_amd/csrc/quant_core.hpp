@@ -164,4 +164,47 @@ __device__ __forceinline__ uint32_t block_byte(float amax, const QuantConsts &qc
   return scale_byte_exact(amax, S);
 }
 
+// ---- branch-free fast paths (the caller settles flagged lanes with the exact functions above) ----
+
+// Scale byte of a block from the bracket alone; `amb` is set when the two bracketing bytes differ
+// (or S is outside the bracket's window), and the returned byte is then not to be used.
+__device__ __forceinline__ uint32_t block_byte_fast(float amax, const QuantConsts &qc, bool &amb) {
+  const float ra = fminf(amax * qc.rlo, kE4M3Max), rb = fminf(amax * qc.rhi, kE4M3Max);
+  const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
+  const uint32_t b0 = pk & 0xffu, b1 = (pk >> 8) & 0xffu;
+  amb = (b0 != b1) || !qc.fast_ok;
+  return b0;  // amax == 0 gives 0 * rlo = 0, byte 0
+}
+
+// Codes of 8 values (nibble i = value i) from the bracket alone, for the block's reciprocal bracket
+// (ilo, ihi); a zero byte passes ilo = ihi = 0, which yields the sign-only codes of a flushed
+// block.  `amb` is set when the two bracketing code words differ.
+__device__ __forceinline__ uint32_t encode8_bracket(const float *v, float ilo, float ihi, bool &amb) {
+  uint32_t lo = 0, hi = 0;
+  lo = fp4_encode2<0>(lo, v[0] * ilo, v[1] * ilo);
+  hi = fp4_encode2<0>(hi, v[0] * ihi, v[1] * ihi);
+  lo = fp4_encode2<1>(lo, v[2] * ilo, v[3] * ilo);
+  hi = fp4_encode2<1>(hi, v[2] * ihi, v[3] * ihi);
+  lo = fp4_encode2<2>(lo, v[4] * ilo, v[5] * ilo);
+  hi = fp4_encode2<2>(hi, v[4] * ihi, v[5] * ihi);
+  lo = fp4_encode2<3>(lo, v[6] * ilo, v[7] * ilo);
+  hi = fp4_encode2<3>(hi, v[6] * ihi, v[7] * ihi);
+  amb = (lo != hi);
+  return lo;
+}
+
+// Codes of 4 values under a nonzero scale byte from the bracket alone; `amb` as above.
+__device__ __forceinline__ uint32_t encode4_fast(const float *v, uint32_t byte, const QuantConsts &qc, bool &amb) {
+  const float e = e4m3_to_f32(byte);
+  const float inv = __builtin_amdgcn_rcpf(e) * qc.invS;
+  const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
+  uint32_t lo = 0, hi = 0;
+  lo = fp4_encode2<0>(lo, v[0] * ilo, v[1] * ilo);
+  hi = fp4_encode2<0>(hi, v[0] * ihi, v[1] * ihi);
+  lo = fp4_encode2<1>(lo, v[2] * ilo, v[3] * ilo);
+  hi = fp4_encode2<1>(hi, v[2] * ihi, v[3] * ihi);
+  amb = (lo != hi) || !qc.fast_ok;
+  return lo;
+}
+
 }  // namespace nvfp4
