@@ -223,7 +223,7 @@ def main():
 DOMINANT = "fc2"  # the block's longest GEMM call (4608 -> 1152)
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fc2_traffic.json")
-KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp")
+KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp", "epilogue.hpp", "quant_core.hpp")  # the dominant GEMM call's code
 
 
 def gemm_kernels(nv, d):
