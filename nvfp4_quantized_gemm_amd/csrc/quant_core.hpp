@@ -193,18 +193,4 @@ __device__ __forceinline__ uint32_t encode8_bracket(const float *v, float ilo, f
   return lo;
 }
 
-// Codes of 4 values under a nonzero scale byte from the bracket alone; `amb` as above.
-__device__ __forceinline__ uint32_t encode4_fast(const float *v, uint32_t byte, const QuantConsts &qc, bool &amb) {
-  const float e = e4m3_to_f32(byte);
-  const float inv = __builtin_amdgcn_rcpf(e) * qc.invS;
-  const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
-  uint32_t lo = 0, hi = 0;
-  lo = fp4_encode2<0>(lo, v[0] * ilo, v[1] * ilo);
-  hi = fp4_encode2<0>(hi, v[0] * ihi, v[1] * ihi);
-  lo = fp4_encode2<1>(lo, v[2] * ilo, v[3] * ilo);
-  hi = fp4_encode2<1>(hi, v[2] * ihi, v[3] * ihi);
-  amb = (lo != hi) || !qc.fast_ok;
-  return lo;
-}
-
 }  // namespace nvfp4
