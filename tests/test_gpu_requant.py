@@ -82,6 +82,8 @@ def run_requant(mode, M, N, K, bias_on, act, s_factor, seed, with_y=True):
     assert bad_s[0].size == 0, f"{bad_s[0].size} scale bytes differ, first at {bad_s[0][0], bad_s[1][0]}"
     bad_p = np.nonzero(gpn != op)
     assert bad_p[0].size == 0, f"{bad_p[0].size} code bytes differ, first at {bad_p[0][0], bad_p[1][0]}"
+    if s_factor > 1e6:
+        assert (os_ == 0).all() and (op != 0).any()  # flushed blocks still carry the signs
     n_sat = int((os_ == 0x7E).sum())
     say(f"  NVFP4 bytes exact ({op.size} code bytes, {os_.size} scale bytes, {n_sat} saturated scales)")
 
@@ -99,6 +101,8 @@ def run_requant(mode, M, N, K, bias_on, act, s_factor, seed, with_y=True):
     (512, 512, 4096, True, nv.ACT_NONE, 3.7),          # split-K: the reduction requantizes
     (1, 64, 256, False, nv.ACT_NONE, 1.0),             # one row
     (64, 96, 48, True, nv.ACT_GELU_TANH, 1.0),         # generic kernel (K % 128 != 0)
+    (300, 272, 384, False, nv.ACT_NONE, 1e7),          # every block flushed: byte 0, sign-only codes
+    (512, 512, 4096, False, nv.ACT_GELU_TANH, 1e7),    # the same in the split-K reduction
 ])
 def test_requant_w4a4(M, N, K, bias_on, act, f):
     run_requant(nv.W4A4, M, N, K, bias_on, act, f, seed=M * 31 + N * 7 + K)
