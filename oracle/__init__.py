@@ -49,6 +49,11 @@ def _load():
     lib.ora_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, ctypes.c_int]
     lib.ora_dequantize.restype = ctypes.c_int
     lib.ora_dequantize.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp, ctypes.c_int]
+    lib.ora_quantize_bs.restype = ctypes.c_int
+    lib.ora_quantize_bs.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp, _vp,
+                                    ctypes.c_int]
+    lib.ora_dequantize_bs.restype = ctypes.c_int
+    lib.ora_dequantize_bs.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, ctypes.c_int, _vp, _vp, ctypes.c_int]
     lib.ora_mx_scale_byte.restype = ctypes.c_int
     lib.ora_mx_scale_byte.argtypes = [ctypes.c_double]
     lib.ora_mx_element_code.restype = ctypes.c_int
@@ -123,37 +128,50 @@ def tensor_scale(x: np.ndarray) -> np.float32:
     return np.float32(out.value)
 
 
-def quantize(x: np.ndarray, S=None, threads: int | None = None):
-    """Quantize x [M, K] (K % 16 == 0).  S=None: dynamic scale; else the given static scale.
+BLOCK_SIZES = (1, 2, 4, 8, 16, 32, 64)  # NVFP4-DiT page, Algorithm 1 / Eq. 9
 
-    Returns (packed uint8 [M, K/2], scales uint8 [M, K/16], S float32).
+
+def quantize(x: np.ndarray, S=None, threads: int | None = None, block: int = 16):
+    """Quantize x [M, K] (K % block == 0, K even).  S=None: dynamic scale; else the given static scale.
+    `block` is the number of consecutive values along K sharing one E4M3 scale byte.
+
+    Returns (packed uint8 [M, K/2], scales uint8 [M, K/block], S float32).
     """
     dtype, M, K, ld = _x_args(x)
-    if K % 16:
-        raise ValueError("K must be a multiple of 16")
+    if block not in BLOCK_SIZES or K % block or K % 2:
+        raise ValueError("K must be a multiple of the block size (and even)")
     if S is None:
         S = tensor_scale(x)
     S = np.float32(S)
     packed = np.empty((M, K // 2), np.uint8)
-    scales = np.empty((M, K // 16), np.uint8)
-    rc = _load().ora_quantize(_ptr(x), dtype, M, K, ld, float(S), _ptr(packed), _ptr(scales),
-                              threads or default_threads())
+    scales = np.empty((M, K // block), np.uint8)
+    if block == 16:
+        rc = _load().ora_quantize(_ptr(x), dtype, M, K, ld, float(S), _ptr(packed), _ptr(scales),
+                                  threads or default_threads())
+    else:
+        rc = _load().ora_quantize_bs(_ptr(x), dtype, M, K, ld, float(S), block, _ptr(packed), _ptr(scales),
+                                     threads or default_threads())
     if rc != 0:
         raise ValueError("precondition failed (non-finite input or invalid S)")
     return packed, scales, S
 
 
 def dequantize(packed: np.ndarray, scales: np.ndarray, S, threads: int | None = None):
-    """Returns (y_f32 float32 [M, K], y_bf16 uint16 [M, K])."""
+    """Returns (y_f32 float32 [M, K], y_bf16 uint16 [M, K]); the block size is K / scales.shape[1]."""
     packed = np.ascontiguousarray(packed, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint8)
     M, K = packed.shape[0], packed.shape[1] * 2
-    if scales.shape != (M, K // 16):
+    if scales.shape[0] != M or scales.shape[1] == 0 or K % scales.shape[1]:
         raise ValueError("scales shape does not match packed")
+    block = K // scales.shape[1]
     y32 = np.empty((M, K), np.float32)
     y16 = np.empty((M, K), np.uint16)
-    rc = _load().ora_dequantize(_ptr(packed), _ptr(scales), float(np.float32(S)), M, K, _ptr(y32), _ptr(y16),
-                                threads or default_threads())
+    if block == 16:
+        rc = _load().ora_dequantize(_ptr(packed), _ptr(scales), float(np.float32(S)), M, K, _ptr(y32), _ptr(y16),
+                                    threads or default_threads())
+    else:
+        rc = _load().ora_dequantize_bs(_ptr(packed), _ptr(scales), float(np.float32(S)), M, K, block, _ptr(y32),
+                                       _ptr(y16), threads or default_threads())
     if rc != 0:
         raise ValueError("precondition failed")
     return y32, y16

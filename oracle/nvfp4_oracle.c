@@ -160,39 +160,53 @@ int ora_element_code(float v, int byte, float S) {
 
 /* ---- quantize / dequantize ---------------------------------------------------------------- */
 
-int ora_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, float S,
-                 uint8_t *packed, uint8_t *scales, int nthreads) {
-  if (K % 16 != 0 || ld < K || !(S >= 0.0f) || !isfinite(S)) return -1;
+/* Block size b (the page's Algorithm 1 / Eq. 9 chooses b from {1, 2, 4, 8, 16, 32, 64} per layer;
+   the format is otherwise unchanged): every run of b consecutive values along K has one E4M3 byte.
+   scales is [M][K/b]. */
+static int valid_block(int64_t K, int b) {
+  return (b == 1 || b == 2 || b == 4 || b == 8 || b == 16 || b == 32 || b == 64) && K % b == 0 && K % 2 == 0;
+}
+
+int ora_quantize_bs(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, float S, int b,
+                    uint8_t *packed, uint8_t *scales, int nthreads) {
+  if (!valid_block(K, b) || ld < K || !(S >= 0.0f) || !isfinite(S)) return -1;
   int bad = 0;
 #ifdef _OPENMP
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16) reduction(| : bad)
 #endif
   for (int64_t i = 0; i < M; ++i) {
-    for (int64_t j = 0; j < K / 16; ++j) {
-      float v[16];
+    for (int64_t j = 0; j < K / b; ++j) {
       double amax = 0.0;
-      for (int t = 0; t < 16; ++t) {
-        v[t] = load_x(x, dtype, i * ld + 16 * j + t);
-        if (!isfinite(v[t])) bad = 1;
-        if (fabs((double)v[t]) > amax) amax = fabs((double)v[t]);
+      for (int t = 0; t < b; ++t) {
+        float v = load_x(x, dtype, i * ld + b * j + t);
+        if (!isfinite(v)) bad = 1;
+        if (fabs((double)v) > amax) amax = fabs((double)v);
       }
       if (amax > 0.0 && S == 0.0f) bad = 1;
       int byte = (amax > 0.0 && S > 0.0f) ? ora_block_scale_byte(amax, S) : 0;
-      scales[i * (K / 16) + j] = (uint8_t)byte;
-      for (int t = 0; t < 16; t += 2) {
-        int c0 = ora_element_code(v[t], byte, S);
-        int c1 = ora_element_code(v[t + 1], byte, S);
-        packed[i * (K / 2) + 8 * j + t / 2] = (uint8_t)(c0 | (c1 << 4));
+      scales[i * (K / b) + j] = (uint8_t)byte;
+      for (int t = 0; t < b; ++t) {
+        int64_t k = b * j + t;
+        int c = ora_element_code(load_x(x, dtype, i * ld + k), byte, S);
+        uint8_t *dst = &packed[i * (K / 2) + k / 2];
+        if (k & 1) *dst = (uint8_t)((*dst & 0x0F) | (c << 4));
+        else *dst = (uint8_t)((*dst & 0xF0) | c);
       }
     }
   }
   return bad ? -1 : 0;
 }
 
-int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K,
-                   float *y_f32, uint16_t *y_bf16, int nthreads) {
-  if (K % 16 != 0 || !isfinite(S)) return -1;
+int ora_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, float S,
+                 uint8_t *packed, uint8_t *scales, int nthreads) {
+  if (K % 16 != 0) return -1;
+  return ora_quantize_bs(x, dtype, M, K, ld, S, 16, packed, scales, nthreads);
+}
+
+int ora_dequantize_bs(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K, int b,
+                      float *y_f32, uint16_t *y_bf16, int nthreads) {
+  if (!valid_block(K, b) || !isfinite(S)) return -1;
   int bad = 0;
 #ifdef _OPENMP
   if (nthreads < 1) nthreads = 1;
@@ -200,7 +214,7 @@ int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_
 #endif
   for (int64_t i = 0; i < M; ++i) {
     for (int64_t k = 0; k < K; ++k) {
-      int byte = scales[i * (K / 16) + k / 16];
+      int byte = scales[i * (K / b) + k / b];
       if ((byte & 0x7F) == 0x7F) bad = 1;
       int code = (packed[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 15;
       double exact = ora_e2m1_value(code) * ora_e4m3_value(byte) * (double)S;
@@ -210,6 +224,12 @@ int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_
     }
   }
   return bad ? -1 : 0;
+}
+
+int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K,
+                   float *y_f32, uint16_t *y_bf16, int nthreads) {
+  if (K % 16 != 0) return -1;
+  return ora_dequantize_bs(packed, scales, S, M, K, 16, y_f32, y_bf16, nthreads);
 }
 
 /* ---- MXFP4 ---------------------------------------------------------------------------------

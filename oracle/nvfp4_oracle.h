@@ -40,6 +40,13 @@ int ora_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, flo
 int ora_dequantize(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K,
                    float *y_f32, uint16_t *y_bf16, int nthreads);
 
+/* The same with block size b in {1, 2, 4, 8, 16, 32, 64} (K % b == 0, K even): one E4M3 byte per
+   b consecutive values along K, scales [M][K/b] [NVFP4-DiT page, Algorithm 1 / Eq. 9 block sizes]. */
+int ora_quantize_bs(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, float S, int b,
+                    uint8_t *packed, uint8_t *scales, int nthreads);
+int ora_dequantize_bs(const uint8_t *packed, const uint8_t *scales, float S, int64_t M, int64_t K, int b,
+                      float *y_f32, uint16_t *y_bf16, int nthreads);
+
 /* MXFP4 (OCP microscaling): 32-value blocks, E8M0 scale X = 2^(floor(log2 amax) - 2), no tensor
    scale; scales are [M][K/32] bytes. */
 int ora_mx_scale_byte(double amax);

@@ -567,3 +567,75 @@ def test_linear_epilogue_bias_per_column():
     np.testing.assert_allclose(oracle.linear_epilogue(Y, b, 1),
                                torch.nn.functional.gelu(torch.from_numpy(Y + b[None, :]), approximate="tanh").numpy(),
                                rtol=1e-14)
+
+
+# ---- block sizes other than 16 (NVFP4-DiT page, Algorithm 1 / Eq. 9: b in {1, 2, ..., 64}) ----------
+
+def brute_quantize_bs(x32, S, b):
+    """The brute-force quantizer with b values per scale byte (independent of the oracle)."""
+    M, K = x32.shape
+    packed = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // b), np.uint8)
+    for i in range(M):
+        for j in range(K // b):
+            blk = [float(v) for v in x32[i, b * j:b * j + b]]
+            byte = brute_scale_byte(max(abs(v) for v in blk), S)
+            scales[i, j] = byte
+            for t, v in enumerate(blk):
+                k = b * j + t
+                packed[i, k // 2] |= brute_code(v, byte, S) << (4 * (k & 1))
+    return packed, scales
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8, 32, 64])
+def test_block_size_quantizer_brute_force(b):
+    """Every block size of the page's set against the exact-rational brute force (dynamic S, a zero
+    block, and a static S small enough to saturate)."""
+    rng = np.random.default_rng(100 + b)
+    for trial in range(4):
+        M, K = int(rng.integers(1, 3)), 64 * int(rng.integers(1, 3))
+        x = (rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        if trial == 1:
+            x[:, :b] = 0.0
+        S = oracle.tensor_scale(x) if trial != 2 else np.float32(oracle.tensor_scale(x) / 64)
+        p, s, _ = oracle.quantize(x, S=S, block=b)
+        bp, bs = brute_quantize_bs(x, float(S), b)
+        np.testing.assert_array_equal(s, bs)
+        np.testing.assert_array_equal(p, bp)
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_block_size_equal_subblock_maxima_reduce_to_b16(b):
+    """Closed form: when every 16-value sub-block of a b-block holds the b-block's maximum magnitude,
+    the b-block's scale byte is each sub-block's byte and the codes are the b = 16 codes."""
+    rng = np.random.default_rng(b)
+    M, K = 8, 4 * b
+    x = rng.uniform(-1.0, 1.0, (M, K)).astype(np.float32)
+    for i in range(M):
+        for j in range(K // b):
+            peak = np.float32(rng.uniform(1.0, 4.0))  # above every other |value| (< 1)
+            for q in range(b // 16):
+                x[i, b * j + 16 * q + int(rng.integers(0, 16))] = peak if q % 2 == 0 else -peak
+    S = oracle.tensor_scale(x)
+    p16, s16, _ = oracle.quantize(x, S=S, block=16)
+    pb, sb, _ = oracle.quantize(x, S=S, block=b)
+    np.testing.assert_array_equal(pb, p16)
+    np.testing.assert_array_equal(np.repeat(sb, b // 16, axis=1), s16)
+
+
+@pytest.mark.parametrize("b", [2, 32, 64])
+def test_block_size_dequantize_exact(b):
+    """Dequantize with b values per byte: each value is RN32(q e S) of its own block's byte, checked
+    against exact rationals."""
+    rng = np.random.default_rng(7 * b)
+    M, K = 3, 128
+    packed = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (M, K // b), dtype=np.uint8)
+    S = np.float32(0.0123)
+    y32, _ = oracle.dequantize(packed, scales, S)
+    for i in range(M):
+        for k in range(K):
+            code = (int(packed[i, k // 2]) >> (4 * (k & 1))) & 15
+            q = Fraction(E2M1_STATED[code & 7]) * (-1 if code & 8 else 1)
+            exact = q * Fraction(E4M3_TORCH[int(scales[i, k // b])]) * Fraction(float(S))
+            assert y32[i, k] == np.float32(float(exact)) or (exact == 0 and y32[i, k] == 0)
