@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
-  NVFP4_ERR_SHAPE = 2,     /* M < 0, N < 0, K < 16, K % 16 != 0, or a size overflow */
+  NVFP4_ERR_SHAPE = 2,     /* M < 0, N < 0, K < 16, K % 16 != 0, a bad block size, or a size overflow */
   NVFP4_ERR_STRIDE = 3,    /* a leading dimension is smaller than the row it must hold */
   NVFP4_ERR_ALIGN = 4,     /* a pointer or row pitch breaks the stated alignment */
   NVFP4_ERR_DTYPE = 5,     /* unknown dtype, or a dtype the call does not accept */
@@ -151,9 +151,9 @@ nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, 
  * to the fp32 accumulator before the output conversion.  Only the summation order differs from
  * the dequantize-then-matmul definition.
  *
- *   mode           NVFP4_W4A4: a = packed [M][lda/2] bytes, a_scales = [M][lda/16] E4M3 bytes,
- *                  a_tensor_scale = device fp32 S_A (as written by nvfp4_quantize; lda == K for
- *                  its output).  lda % 16 == 0, lda >= K.
+ *   mode           NVFP4_W4A4: a = packed [M][lda/2] bytes (8-byte aligned), a_scales = [M][lda/16]
+ *                  E4M3 bytes (4-byte aligned), a_tensor_scale = device fp32 S_A (as written by
+ *                  nvfp4_quantize; lda == K for its output).  lda % 16 == 0, lda >= K.
  *                  NVFP4_W4A16: a = bf16 [M][lda] (lda >= K, lda * 2 % 16 == 0, 16-byte aligned);
  *                  a_scales and a_tensor_scale must be NULL.
  *   b_prepacked    weight from nvfp4_prepack_weight(N, K); b_tensor_scale its device fp32 S_B.
@@ -167,6 +167,36 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
                           const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
                           int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Other block sizes [NVFP4-DiT page, Methodology section 2, Algorithm 1 / Eq. 9 (a block size per
+ * layer from {1, ..., 64}) and the configuration table (a fixed block size)].  block_size =
+ * values per E4M3 scale byte along K, one of 16, 32, 64; K % block_size == 0; scales are then
+ * [rows][K / block_size] bytes.  Everything else (tensor scale, rounding, packing, layouts,
+ * alignments, errors) is as for the calls without the suffix, which are these with block_size 16.
+ * A weight prepacked with any block size is read by every GEMM call the same way (its scales are
+ * expanded to one byte per 16 k); a_block_size is the W4A4 activation's block size (lda must be a
+ * multiple of it) and is ignored for W4A16.  nvfp4_gemm* also need a_scales 4-byte aligned.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                 nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream);
+nvfp4_status_t nvfp4_dequantize_bs(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                   int64_t M, int64_t K, int block_size, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                   void *stream);
+nvfp4_status_t nvfp4_fake_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                      int block_size, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                      float *tensor_scale, nvfp4_scale_mode_t mode, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+nvfp4_status_t nvfp4_prepack_weight_bs(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                                       int block_size, void *prepacked, void *stream);
+nvfp4_status_t nvfp4_unpack_weight_bs(const void *prepacked, int64_t N, int64_t K, int block_size, uint8_t *packed,
+                                      uint8_t *scales, void *stream);
+nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                             const float *a_tensor_scale, int a_block_size, const void *b_prepacked,
+                             const float *b_tensor_scale, int64_t M, int64_t N, int64_t K, int64_t lda, void *c,
+                             nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * GEMM with NVFP4 output (epilogue-fused requantization) [NVFP4-DiT page, Methodology section 3:
@@ -200,6 +230,14 @@ nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_
                                   int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,
                                   const float *out_tensor_scale, uint8_t *out_packed, uint8_t *out_scales, float *y,
                                   int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream);
+/* The same with the W4A4 activation's block size (see the block-size calls above); the output is
+   written with 16-value blocks. */
+nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                                     const float *a_tensor_scale, int a_block_size, const void *b_prepacked,
+                                     const float *b_tensor_scale, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                     const float *bias, nvfp4_act_t act, const float *out_tensor_scale,
+                                     uint8_t *out_packed, uint8_t *out_scales, float *y, int64_t ld_y, void *workspace,
+                                     size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * MXFP4, the related microscaling format (vllm-omni RFC, Motivation; the pages do not define it,

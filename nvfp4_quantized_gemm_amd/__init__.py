@@ -41,6 +41,8 @@ EXPORTED = (
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
     "nvfp4_gemm_requant_workspace_bytes", "nvfp4_gemm_requant",
+    "nvfp4_quantize_bs", "nvfp4_dequantize_bs", "nvfp4_fake_quantize_bs", "nvfp4_prepack_weight_bs",
+    "nvfp4_unpack_weight_bs", "nvfp4_gemm_bs", "nvfp4_gemm_requant_bs",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
 )
 
@@ -90,6 +92,21 @@ def lib():
     L.nvfp4_gemm_requant.restype = _i
     L.nvfp4_gemm_requant.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _vp, _vp, _vp,
                                      _vp, _i64, _vp, _sz, _vp]
+    L.nvfp4_quantize_bs.restype = _i
+    L.nvfp4_quantize_bs.argtypes = [_vp, _i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+    L.nvfp4_fake_quantize_bs.restype = _i
+    L.nvfp4_fake_quantize_bs.argtypes = [_vp, _i, _i64, _i64, _i64, _i, _vp, _i, _i64, _vp, _i, _vp, _sz, _vp]
+    L.nvfp4_dequantize_bs.restype = _i
+    L.nvfp4_dequantize_bs.argtypes = [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _i64, _vp]
+    L.nvfp4_prepack_weight_bs.restype = _i
+    L.nvfp4_prepack_weight_bs.argtypes = [_vp, _vp, _i64, _i64, _i, _vp, _vp]
+    L.nvfp4_unpack_weight_bs.restype = _i
+    L.nvfp4_unpack_weight_bs.argtypes = [_vp, _i64, _i64, _i, _vp, _vp, _vp]
+    L.nvfp4_gemm_bs.restype = _i
+    L.nvfp4_gemm_bs.argtypes = [_i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _i64, _vp, _sz, _vp]
+    L.nvfp4_gemm_requant_bs.restype = _i
+    L.nvfp4_gemm_requant_bs.argtypes = [_i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _vp, _vp,
+                                        _vp, _vp, _i64, _vp, _sz, _vp]
     L.nvfp4_mx_quantize.restype = _i
     L.nvfp4_mx_quantize.argtypes = [_vp, _i, _i64, _i64, _i64, _vp, _vp, _vp]
     L.nvfp4_mx_dequantize.restype = _i
@@ -138,19 +155,19 @@ def nvfp4_quantize_workspace_bytes(M: int, K: int) -> int:
 
 
 def nvfp4_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *, static: bool | None = None,
-                   packed=None, scales=None, workspace=None, stream=None):
+                   packed=None, scales=None, workspace=None, block_size: int = 16, stream=None):
     """Quantize x [M, K] (fp32 or bf16, device).
 
     static=False (the default when tensor_scale is None): dynamic scale, computed on the device and
     written to tensor_scale (allocated when None).  static=True (the default when tensor_scale is
-    given): tensor_scale holds the caller's S.  Returns (packed u8 [M, K/2], scales u8 [M, K/16],
-    S f32 [1])."""
+    given): tensor_scale holds the caller's S.  block_size: values per scale byte (16, 32 or 64).
+    Returns (packed u8 [M, K/2], scales u8 [M, K/block_size], S f32 [1])."""
     M, K, ld = _rows(x, "x")
     dev = x.device
     if packed is None:
         packed = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((M, max(K // 16, 0)), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, max(K // block_size, 0)), dtype=torch.uint8, device=dev)
     if static is None:
         static = tensor_scale is not None
     dynamic = not static
@@ -165,27 +182,35 @@ def nvfp4_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *,
         if workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), M, K, ld, _ptr(packed), _ptr(scales), _ptr(S),
-                              SCALE_DYNAMIC if dynamic else SCALE_STATIC, _ptr(workspace), ws_bytes,
-                              _stream(stream))
-    _check(st, "nvfp4_quantize")
+    st = lib().nvfp4_quantize_bs(_ptr(x), _dtype_code(x.dtype), M, K, ld, block_size, _ptr(packed), _ptr(scales),
+                                 _ptr(S), SCALE_DYNAMIC if dynamic else SCALE_STATIC, _ptr(workspace), ws_bytes,
+                                 _stream(stream))
+    _check(st, "nvfp4_quantize_bs")
     return packed, scales, S
+
+
+def _block_of(K: int, scales: torch.Tensor) -> int:
+    """Block size of a canonical scale tensor [rows, K / block_size]."""
+    n = scales.shape[1] if scales.dim() == 2 else 0
+    return K // n if n else 16
 
 
 def nvfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor,
                      dtype: torch.dtype = torch.float32, *, out=None, stream=None) -> torch.Tensor:
+    """y = dequantize(packed, scales, S); the block size is read from the shape of scales."""
     M, K = packed.shape[0], packed.shape[1] * 2
     if out is None:
         out = torch.empty((M, K), dtype=dtype, device=packed.device)
     _, _, ld = _rows(out, "out")
-    st = lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), _ptr(tensor_scale), M, K, _ptr(out),
-                                _dtype_code(out.dtype), ld, _stream(stream))
-    _check(st, "nvfp4_dequantize")
+    st = lib().nvfp4_dequantize_bs(_ptr(packed), _ptr(scales), _ptr(tensor_scale), M, K, _block_of(K, scales),
+                                   _ptr(out), _dtype_code(out.dtype), ld, _stream(stream))
+    _check(st, "nvfp4_dequantize_bs")
     return out
 
 
 def nvfp4_fake_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *, static: bool | None = None,
-                        out_dtype: torch.dtype | None = None, out=None, workspace=None, stream=None):
+                        out_dtype: torch.dtype | None = None, out=None, workspace=None, block_size: int = 16,
+                        stream=None):
     """y = dequantize(quantize(x)) in one pass (x [M, K] fp32 or bf16 on the device).  Scale
     arguments as for nvfp4_quantize.  Returns (y, S)."""
     M, K, ld = _rows(x, "x")
@@ -205,10 +230,11 @@ def nvfp4_fake_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = Non
         if workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_fake_quantize(_ptr(x), _dtype_code(x.dtype), M, K, ld, _ptr(out), _dtype_code(out.dtype), ld_y,
-                                   _ptr(tensor_scale), SCALE_STATIC if static else SCALE_DYNAMIC, _ptr(workspace),
-                                   ws_bytes, _stream(stream))
-    _check(st, "nvfp4_fake_quantize")
+    st = lib().nvfp4_fake_quantize_bs(_ptr(x), _dtype_code(x.dtype), M, K, ld, block_size, _ptr(out),
+                                      _dtype_code(out.dtype), ld_y, _ptr(tensor_scale),
+                                      SCALE_STATIC if static else SCALE_DYNAMIC, _ptr(workspace), ws_bytes,
+                                      _stream(stream))
+    _check(st, "nvfp4_fake_quantize_bs")
     return out, tensor_scale
 
 
@@ -217,19 +243,19 @@ class FakeQuantizeSTE(torch.autograd.Function):
     in x's dtype), backward is the straight-through estimator, i.e. the incoming gradient unchanged."""
 
     @staticmethod
-    def forward(ctx, x, tensor_scale=None):
-        y, _ = nvfp4_fake_quantize(x.contiguous(), tensor_scale)
+    def forward(ctx, x, tensor_scale=None, block_size=16):
+        y, _ = nvfp4_fake_quantize(x.contiguous(), tensor_scale, block_size=block_size)
         return y
 
     @staticmethod
     def backward(ctx, grad_out):
-        return grad_out, None
+        return grad_out, None, None
 
 
-def fake_quantize_ste(x: torch.Tensor, tensor_scale: torch.Tensor | None = None) -> torch.Tensor:
+def fake_quantize_ste(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, block_size: int = 16) -> torch.Tensor:
     """NVFP4 fake quantization with a straight-through gradient (dynamic scale when tensor_scale is
-    None, else the given static scale)."""
-    return FakeQuantizeSTE.apply(x, tensor_scale)
+    None, else the given static scale; block_size values per scale byte: 16, 32 or 64)."""
+    return FakeQuantizeSTE.apply(x, tensor_scale, block_size)
 
 
 # ---- weight prepack -------------------------------------------------------------------------------
@@ -243,16 +269,18 @@ def nvfp4_prepack_weight(packed: torch.Tensor, scales: torch.Tensor, *, out=None
     nbytes = nvfp4_prepacked_bytes(N, K)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
-    st = lib().nvfp4_prepack_weight(_ptr(packed), _ptr(scales), N, K, _ptr(out), _stream(stream))
-    _check(st, "nvfp4_prepack_weight")
+    st = lib().nvfp4_prepack_weight_bs(_ptr(packed), _ptr(scales), N, K, _block_of(K, scales), _ptr(out),
+                                       _stream(stream))
+    _check(st, "nvfp4_prepack_weight_bs")
     return out
 
 
-def nvfp4_unpack_weight(prepacked: torch.Tensor, N: int, K: int, *, stream=None):
+def nvfp4_unpack_weight(prepacked: torch.Tensor, N: int, K: int, *, block_size: int = 16, stream=None):
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=prepacked.device)
-    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=prepacked.device)
-    st = lib().nvfp4_unpack_weight(_ptr(prepacked), N, K, _ptr(packed), _ptr(scales), _stream(stream))
-    _check(st, "nvfp4_unpack_weight")
+    scales = torch.empty((N, K // block_size), dtype=torch.uint8, device=prepacked.device)
+    st = lib().nvfp4_unpack_weight_bs(_ptr(prepacked), N, K, block_size, _ptr(packed), _ptr(scales),
+                                      _stream(stream))
+    _check(st, "nvfp4_unpack_weight_bs")
     return packed, scales
 
 
@@ -265,13 +293,16 @@ def nvfp4_gemm_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
 def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked: torch.Tensor,
                b_tensor_scale: torch.Tensor, N: int, K: int, out_dtype: torch.dtype = torch.bfloat16, *,
                out=None, workspace=None, stream=None) -> torch.Tensor:
-    """Y = A B^T.  W4A4: a = packed u8 [M, K/2] with a_scales u8 [M, K/16] and a_tensor_scale
-    (from nvfp4_quantize).  W4A16: a = bf16 [M, K], a_scales = a_tensor_scale = None."""
+    """Y = A B^T.  W4A4: a = packed u8 [M, K/2] with a_scales u8 [M, K/block] and a_tensor_scale
+    (from nvfp4_quantize; the block size is read from the shape of a_scales).  W4A16: a = bf16
+    [M, K], a_scales = a_tensor_scale = None."""
     M = a.shape[0]
     if mode == W4A4:
         lda = a.stride(0) * 2
+        ablk = _block_of(lda, a_scales)
     else:
         _, _, lda = _rows(a, "a")
+        ablk = 16
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     ldc = out.stride(0)
@@ -279,10 +310,10 @@ def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_gemm(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_prepacked),
-                          _ptr(b_tensor_scale), M, N, K, lda, _ptr(out), _dtype_code(out.dtype), ldc,
-                          _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "nvfp4_gemm")
+    st = lib().nvfp4_gemm_bs(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), ablk, _ptr(b_prepacked),
+                             _ptr(b_tensor_scale), M, N, K, lda, _ptr(out), _dtype_code(out.dtype), ldc,
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_gemm_bs")
     return out
 
 
@@ -303,8 +334,10 @@ def nvfp4_gemm_requant(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_p
     M = a.shape[0]
     if mode == W4A4:
         lda = a.stride(0) * 2
+        ablk = _block_of(lda, a_scales)
     else:
         _, _, lda = _rows(a, "a")
+        ablk = 16
     if packed is None:
         packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
     if scales is None:
@@ -314,11 +347,11 @@ def nvfp4_gemm_requant(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_p
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_gemm_requant(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_prepacked),
-                                  _ptr(b_tensor_scale), M, N, K, lda, _ptr(bias), act, _ptr(out_tensor_scale),
-                                  _ptr(packed), _ptr(scales), _ptr(y), ldy, _ptr(workspace), ws_bytes,
-                                  _stream(stream))
-    _check(st, "nvfp4_gemm_requant")
+    st = lib().nvfp4_gemm_requant_bs(mode, _ptr(a), _ptr(a_scales), _ptr(a_tensor_scale), ablk, _ptr(b_prepacked),
+                                     _ptr(b_tensor_scale), M, N, K, lda, _ptr(bias), act, _ptr(out_tensor_scale),
+                                     _ptr(packed), _ptr(scales), _ptr(y), ldy, _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    _check(st, "nvfp4_gemm_requant_bs")
     return packed, scales
 
 

@@ -113,9 +113,22 @@ __device__ __forceinline__ void grouped_tile(int j, int tiles_m, int tiles_n, in
   tn = r / gm;
 }
 
-// Lane swap across quads: lane i reads lane i ^ 4 (ds_swizzle bit mode, xor mask 4).
+// Lane swaps across quads: lane i reads lane i ^ 4, or lane i ^ 8 (ds_swizzle bit mode, xor masks).
 __device__ __forceinline__ float swap_lane4(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+__device__ __forceinline__ float swap_lane8(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+}
+
+// Maximum over the LPB adjacent lanes of an aligned group (LPB = 1, 2, 4, 8 or 16).
+template <int LPB>
+__device__ __forceinline__ float group_max(float v) {
+  if (LPB >= 2) v = fmaxf(v, swap_lane1(v));
+  if (LPB >= 4) v = fmaxf(v, swap_lane2(v));
+  if (LPB >= 8) v = fmaxf(v, swap_lane4(v));
+  if (LPB >= 16) v = fmaxf(v, swap_lane8(v));
+  return v;
 }
 
 // Lane-contiguous element mapping of the bandwidth kernels.  A tensor of M rows x K (K a multiple
@@ -126,9 +139,10 @@ __device__ __forceinline__ float swap_lane4(float v) {
 template <int EPL, int BLK = 16>
 struct Segments {
   static constexpr int kLanesPerBlock = BLK / EPL;
-  static constexpr int kShift = (kLanesPerBlock == 2) ? 1 : (kLanesPerBlock == 4) ? 2 : 3;
+  static constexpr int kShift = (kLanesPerBlock == 2) ? 1 : (kLanesPerBlock == 4) ? 2 : (kLanesPerBlock == 8) ? 3 : 4;
   static_assert(EPL == 8 || EPL == 4, "segments are 8 or 4 elements");
-  static_assert(kLanesPerBlock == 2 || kLanesPerBlock == 4 || kLanesPerBlock == 8, "lanes per block");
+  static_assert(kLanesPerBlock == 2 || kLanesPerBlock == 4 || kLanesPerBlock == 8 || kLanesPerBlock == 16,
+                "lanes per block");
   // element offset of segment g in a tensor with row stride ld (elements); rows of exactly K
   // elements (DENSE) need no division, otherwise bpr divides by the blocks per row
   template <bool DENSE>

@@ -15,13 +15,13 @@ namespace {
 constexpr int kSegsPerLane = 4;
 }
 
-template <int OUT, bool DENSE>
+template <int OUT, bool DENSE, int BLK>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ packed,
                                                     const uint8_t *__restrict__ scales,
                                                     const float *__restrict__ tensor_scale, uint64_t nseg,
                                                     FastDiv bpr, void *__restrict__ y, int64_t ld_y) {
   constexpr int E = (OUT == 1) ? 8 : 4;  // values per lane segment
-  using Map = Segments<E>;
+  using Map = Segments<E, BLK>;  // a segment's block scale is byte g / Map::kLanesPerBlock
   constexpr int U = kSegsPerLane;
   const float S = *tensor_scale;
   const int lane = threadIdx.x & 63;
@@ -79,22 +79,30 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
   }
 }
 
+template <int BLK>
+static void run_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t K,
+                           uint64_t nseg, unsigned grid, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / BLK));
+  const bool dense = (ld_y == K);
+  if (out_dtype == 0) {
+    if (dense) k_dequantize<0, true, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<0, false, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+  } else {
+    if (dense) k_dequantize<1, true, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<1, false, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+  }
+}
+
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
-                             int64_t K, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
-  const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
+                             int64_t K, int blk, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
   const uint64_t nseg = (uint64_t)M * (uint64_t)K / (out_dtype == 0 ? 4u : 8u);
   const uint64_t tiles = (nseg + 64 * kSegsPerLane - 1) / (64 * kSegsPerLane);
   uint64_t g = (tiles + 3) / 4;
   if (g < 1) g = 1;
   if (g > (uint64_t)kDequantizeMaxGrid) g = kDequantizeMaxGrid;
-  const bool dense = (ld_y == K);
-  if (out_dtype == 0) {
-    if (dense) k_dequantize<0, true><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-    else k_dequantize<0, false><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-  } else {
-    if (dense) k_dequantize<1, true><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-    else k_dequantize<1, false><<<(unsigned)g, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-  }
+  if (blk == 32) run_dequantize<32>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
+  else if (blk == 64) run_dequantize<64>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
+  else run_dequantize<16>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
   return hipGetLastError();
 }
 

@@ -89,7 +89,10 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // M and columns past N are clamped to the last valid one (their results are never stored).
 // Per chunk a wave first reads all of its fragments for the chunk into registers, then issues the
 // next chunk's loads into the other buffer, then runs its 8 MFMA steps from registers.
-template <int MODE, int BM, int BN, int WM, int WN, int OUT>
+// ABLK: values per A scale byte along K (16, 32 or 64; W4A4).  Lane l = r + 32 h needs the bytes of
+// the blocks under its 64 k of a chunk: 4, 2 or 1 bytes, fetched as the aligned dword holding them
+// and shifted into place when read.
+template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
@@ -138,7 +141,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // The host guarantees BM * (A row bytes) < 2^31, so the A lane offsets fit in 32 bits.
   const int64_t arow_bytes = (MODE == 0) ? lda / 2 : lda * 2;
   const uint8_t *a_tile = static_cast<const uint8_t *>(a) + (int64_t)m0 * arow_bytes;
-  const uint8_t *as_tile = (MODE == 0) ? a_scales + (int64_t)m0 * (lda / 16) : nullptr;
+  static_assert(ABLK == 16 || ABLK == 32 || ABLK == 64, "A block size");
+  const uint8_t *as_tile = (MODE == 0) ? a_scales + (int64_t)m0 * (lda / ABLK) : nullptr;
   uint32_t oa[NA / 4];
   uint32_t oas[NAS / 4 > 0 ? NAS / 4 : 1];
 #pragma unroll
@@ -158,7 +162,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < NAS / 4; ++i) {
     const int q = wave + 4 * i;
     const int row = min(m0 + q * 32 + lr, M - 1) - m0;
-    oas[i] = (uint32_t)(row * (uint32_t)(lda / 16)) + 4 * lh;
+    // byte index (in the tile's scale rows) of the lane's first block in chunk 0: 16-blocks are
+    // dword aligned (lda % 64 == 0), 32-blocks come as the row's dword per chunk (the lane's pair
+    // is bytes 2h, 2h + 1), a 64-block's byte sits at a chunk-dependent position in its dword
+    oas[i] = (uint32_t)(row * (uint32_t)(lda / ABLK)) + (ABLK == 16 ? 4 * lh : (ABLK == 64 ? lh : 0));
   }
   const uint32_t ob = lane * 16, obs = lane * 4;
   // prepacked B unit (n-unit nu, chunk kc) of this wave's q-th block
@@ -173,7 +180,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       g2l16(a_tile + (int64_t)kc * kAStep + oa[t], st + (wave + 4 * t) * 1024);
     } else if (t < NA / 4 + NAS / 4) {
       const int i = t - NA / 4;
-      g2l4(as_tile + kc * 8 + oas[i], st + Cfg::kALds + (wave + 4 * i) * 256);
+      if constexpr (ABLK == 64)
+        g2l4(as_tile + ((oas[i] + 2u * (uint32_t)kc) & ~3u), st + Cfg::kALds + (wave + 4 * i) * 256);
+      else
+        g2l4(as_tile + kc * (128 / ABLK) + oas[i], st + Cfg::kALds + (wave + 4 * i) * 256);
     } else if (t < NA / 4 + NAS / 4 + NB / 4) {
       const int i = t - NA / 4 - NAS / 4, q = wave + 4 * i;
       g2l16(bp + b_unit(q >> 1, kc) * 2048ull + (q & 1) * 1024 + ob,
@@ -227,12 +237,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         rb[j] = *reinterpret_cast<const u32x4 *>(st + Cfg::kALds + Cfg::kASLds + ((unit * 2 + part) * 64 + lane) * 16);
       }
     };
-    auto read_scales = [&](int buf) {
+    // kabs: the absolute chunk whose data the stage holds (it fixes a 64-block's byte position)
+    auto read_scales = [&](int buf, int kabs) {
       const uint8_t *st = stage(buf);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int sub = wm * (BM / WM / 32) + i;
-        Sa[i] = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + (sub * 64 + lane) * 4);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + (sub * 64 + lane) * 4);
+        if constexpr (ABLK == 16) {
+          Sa[i] = w;
+        } else if constexpr (ABLK == 32) {
+          Sa[i] = w >> (16 * lh);
+        } else {
+          // the byte position of the row being read (this wave's sub-tile, not the rows this wave
+          // fetched), exactly as the fetch computed it
+          const uint32_t row = (uint32_t)(min(m0 + sub * 32 + lr, M - 1) - m0);
+          Sa[i] = w >> (8 * ((row * (uint32_t)(lda / ABLK) + lh + 2u * (uint32_t)kabs) & 3u));
+        }
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -264,7 +285,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto mul_step = [&](f16x2 (*ea)[2], f16x2 (*eb)[2], int s) {
       const int blk = s >> 1, slot = s & 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) Fa[slot][i] = scale_f16x8(Qa[slot][i], ea[i][blk >> 1][blk & 1]);
+      for (int i = 0; i < TM; ++i) {
+        // the lane's byte for step s: 16-blocks: s / 2 of 4; 32-blocks: s / 4 of 2; 64: the one
+        const _Float16 e = (ABLK == 16) ? ea[i][blk >> 1][blk & 1] : (ABLK == 32 ? ea[i][0][s >> 2] : ea[i][0][0]);
+        Fa[slot][i] = scale_f16x8(Qa[slot][i], e);
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j) Fb[slot][j] = scale_f16x8(Qb[slot][j], eb[j][blk >> 1][blk & 1]);
     };
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       wait_vmem_then_barrier<0>();
     }
     read_part(P0a, P0b, 0, 0);
-    read_scales(0);
+    read_scales(0, kbeg);
     cvt_scales(Ea, Eb);
     cvt_step(P0a, P0b, 0);
     cvt_step(P0a, P0b, 1);
@@ -333,7 +358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           if (s * kPer + u < NSLOT) issue_slot(kdma, bdma, s * kPer + u);
         if (s == 3) {
           read_part(P0a, P0b, bnext, 0);  // P0 of this chunk was last decoded in step 1
-          read_scales(bnext);
+          read_scales(bnext, kbeg + min(kc + 1, nk - 1));
         }
         if (s == 6) cvt_scales(Na, Nb);
         // stage 2 for step s+1, stage 1 for step s+2 (steps 8 and 9 are the next chunk's 0 and 1)
@@ -464,7 +489,7 @@ template <int MODE, int OUT>
 __global__ __launch_bounds__(256) void k_gemm_generic(const void *__restrict__ a, const uint8_t *__restrict__ a_scales,
                                                       const float *__restrict__ a_ts, const uint8_t *__restrict__ bp,
                                                       const float *__restrict__ b_ts, int64_t M, int64_t N, int64_t K,
-                                                      int64_t lda, void *__restrict__ c, int64_t ldc) {
+                                                      int64_t lda, int ablk, void *__restrict__ c, int64_t ldc) {
   const int64_t Kc = (K + 127) / 128, Nu = (N + 31) / 32;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
@@ -477,7 +502,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const void *__restrict__ a
         const uint8_t cb = static_cast<const uint8_t *>(a)[m * (lda / 2) + (k >> 1)];
         const uint32_t code = (k & 1) ? (cb >> 4) : (cb & 15u);
         const f32x2 q = fp4_decode2_f32<0>(code);
-        av = q.x * e4m3_to_f32(a_scales[m * (lda / 16) + (k >> 4)]);
+        av = q.x * e4m3_to_f32(a_scales[m * (lda / ablk) + k / ablk]);
       } else {
         av = __uint_as_float((uint32_t) static_cast<const uint16_t *>(a)[m * lda + k] << 16);
       }
@@ -567,12 +592,12 @@ hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int
 
 // ---- launchers ----------------------------------------------------------------------------------
 
-template <int MODE, int BM, int BN, int WM, int WN, int OUT>
+template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK = 16>
 static hipError_t launch_tiled(const GemmArgs &g, int m_off, int n_off, int m_len, int n_len, int splits,
                                float *partial, hipStream_t stream) {
   using Cfg = TileCfg<MODE, BM, BN>;
   const int tm = (m_len + BM - 1) / BM, tn = (n_len + BN - 1) / BN;
-  auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT>;
+  auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT, ABLK>;
   const int smem = 3 * Cfg::kStage;
   static bool configured = false;  // per instantiation
   if (!configured) {
@@ -594,7 +619,7 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
   if (grid > 65536) grid = 65536;
   k_gemm_generic<MODE, OUT><<<(unsigned)grid, 256, 0, stream>>>(g.a, g.a_scales, g.a_ts,
                                                                  static_cast<const uint8_t *>(g.b), g.b_ts, g.M, g.N,
-                                                                 g.K, g.lda, g.c, g.ldc);
+                                                                 g.K, g.lda, g.a_blk, g.c, g.ldc);
   return hipGetLastError();
 }
 
@@ -666,26 +691,26 @@ size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
   return pl.splits > 1 ? (size_t)pl.splits * mn : 0;
 }
 
-template <int OUT>
+template <int OUT, int ABLK>
 static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t stream) {
   const int M = (int)g.M, N = (int)g.N;
   switch (pl.variant) {
     case GemmVariant::W4A4_256x256: {
       if (pl.splits > 1) {
         float *part = static_cast<float *>(g.workspace);
-        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT, ABLK>(g, 0, 0, M, N, pl.splits, part, stream);
         if (e != hipSuccess) return e;
         return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, g.qo, stream);
       }
       if (pl.n_big > 0 && pl.n_big < N) {
-        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, (int)pl.n_big, 1, nullptr, stream);
+        hipError_t e = launch_tiled<0, 256, 256, 2, 2, OUT, ABLK>(g, 0, 0, M, (int)pl.n_big, 1, nullptr, stream);
         if (e != hipSuccess) return e;
-        return launch_tiled<0, 128, 128, 2, 2, OUT>(g, 0, (int)pl.n_big, M, N - (int)pl.n_big, 1, nullptr, stream);
+        return launch_tiled<0, 128, 128, 2, 2, OUT, ABLK>(g, 0, (int)pl.n_big, M, N - (int)pl.n_big, 1, nullptr, stream);
       }
-      return launch_tiled<0, 256, 256, 2, 2, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+      return launch_tiled<0, 256, 256, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A4_128x128:
-      return launch_tiled<0, 128, 128, 2, 2, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+      return launch_tiled<0, 128, 128, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
     case GemmVariant::W4A16_128x256: {
       if (pl.splits > 1) {
         float *part = static_cast<float *>(g.workspace);
@@ -703,6 +728,14 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
   }
 }
 
+// W4A4 plans are instantiated per A block size; W4A16 has no A scales
+template <int OUT>
+static hipError_t run_plan_blk(const GemmArgs &g, const GemmPlan &pl, hipStream_t stream) {
+  if (g.mode == 0 && g.a_blk == 32) return run_plan<OUT, 32>(g, pl, stream);
+  if (g.mode == 0 && g.a_blk == 64) return run_plan<OUT, 64>(g, pl, stream);
+  return run_plan<OUT, 16>(g, pl, stream);
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
   const GemmPlan pl = plan_gemm(g.mode, g.M, g.N, g.K, g.lda);
   if (g.out_dtype == 2) {
@@ -718,13 +751,13 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
       return launch_splitk_reduce(static_cast<const float *>(g.workspace), 1, g.M, g.N, nullptr, 2, 0, nullptr,
                                   nullptr, g.qo, stream);
     }
-    return run_plan<2>(g, pl, stream);
+    return run_plan_blk<2>(g, pl, stream);
   }
   if (pl.variant == GemmVariant::Generic) {
     if (g.mode == 0) return g.out_dtype == 0 ? launch_generic<0, 0>(g, stream) : launch_generic<0, 1>(g, stream);
     return g.out_dtype == 0 ? launch_generic<1, 0>(g, stream) : launch_generic<1, 1>(g, stream);
   }
-  return g.out_dtype == 0 ? run_plan<0>(g, pl, stream) : run_plan<1>(g, pl, stream);
+  return g.out_dtype == 0 ? run_plan_blk<0>(g, pl, stream) : run_plan_blk<1>(g, pl, stream);
 }
 
 }  // namespace nvfp4

@@ -9,19 +9,21 @@ constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pa
 constexpr int kQuantizeMaxGrid = 2048;  // grid cap of the quantize kernel (grid-stride beyond)
 constexpr int kDequantizeMaxGrid = 4096;
 
-hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+// blk: values per E4M3 scale byte along K (16, 32 or 64)
+hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, uint8_t *packed,
                            uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, hipStream_t stream);
 // Fake quantization: y = dequantize(quantize(x)) in one pass (no NVFP4 tensor is written).
-hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, void *y, int y_dtype,
-                                int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
+hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, void *y,
+                                int y_dtype, int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
                                 hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
-                             int64_t K, void *y, int out_dtype, int64_t ld_y, hipStream_t stream);
+                             int64_t K, int blk, void *y, int out_dtype, int64_t ld_y, hipStream_t stream);
 
-hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, void *out,
+hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, int blk, void *out,
                           hipStream_t stream);
-hipError_t launch_unpack(const void *in, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales, hipStream_t stream);
+hipError_t launch_unpack(const void *in, int64_t N, int64_t K, int blk, uint8_t *packed, uint8_t *scales,
+                         hipStream_t stream);
 
 enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256, W4A16_Skinny };
 
@@ -50,6 +52,7 @@ struct GemmArgs {
   int mode;  // 0 W4A4, 1 W4A16
   const void *a;
   const uint8_t *a_scales;
+  int a_blk = 16;  // W4A4: values per A scale byte along K (16, 32 or 64)
   const float *a_ts;
   const void *b;
   const float *b_ts;

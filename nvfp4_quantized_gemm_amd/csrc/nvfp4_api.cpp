@@ -24,6 +24,13 @@ nvfp4_status_t check_mk(int64_t M, int64_t K) {
   return NVFP4_OK;
 }
 
+// Block size: values per E4M3 scale byte along K (16, 32 or 64), K a multiple of it.
+nvfp4_status_t check_bs(int64_t K, int bs) {
+  if (bs != 16 && bs != 32 && bs != 64) return NVFP4_ERR_SHAPE;
+  if (K % bs != 0) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
 int elem_size(nvfp4_dtype_t t) { return t == NVFP4_F32 ? 4 : 2; }
 bool valid_dtype(int t) { return t == NVFP4_F32 || t == NVFP4_BF16; }
 
@@ -71,13 +78,15 @@ size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K) {
   return (size_t)kAmaxPartials * sizeof(float);
 }
 
-nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
-                              uint8_t *packed, uint8_t *scales, float *tensor_scale, nvfp4_scale_mode_t mode,
-                              void *workspace, size_t workspace_bytes, void *stream) {
+nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                 nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
   if (!tensor_scale) return NVFP4_ERR_NULL;
   if (!valid_dtype(x_dtype)) return NVFP4_ERR_DTYPE;
   if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
   nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  st = check_bs(K, block_size);
   if (st != NVFP4_OK) return st;
   if (M > 0 && (!x || !packed || !scales)) return NVFP4_ERR_NULL;
   if (M == 0 && mode == NVFP4_SCALE_STATIC) return NVFP4_OK;  // nothing to read or write
@@ -91,18 +100,28 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, i
   }
   st = check_device();
   if (st != NVFP4_OK) return st;
-  return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, packed, scales, tensor_scale,
+  return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale,
                                     mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
                                     static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status_t nvfp4_fake_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
-                                   void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, float *tensor_scale,
-                                   nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
+nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                              uint8_t *packed, uint8_t *scales, float *tensor_scale, nvfp4_scale_mode_t mode,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return nvfp4_quantize_bs(x, x_dtype, M, K, ld_x, 16, packed, scales, tensor_scale, mode, workspace, workspace_bytes,
+                           stream);
+}
+
+nvfp4_status_t nvfp4_fake_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                      int block_size, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                      float *tensor_scale, nvfp4_scale_mode_t mode, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
   if (!tensor_scale) return NVFP4_ERR_NULL;
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
   if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
   nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  st = check_bs(K, block_size);
   if (st != NVFP4_OK) return st;
   if (M > 0 && (!x || !y)) return NVFP4_ERR_NULL;
   if (M == 0 && mode == NVFP4_SCALE_STATIC) return NVFP4_OK;  // nothing to read or write
@@ -116,15 +135,25 @@ nvfp4_status_t nvfp4_fake_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t
   }
   st = check_device();
   if (st != NVFP4_OK) return st;
-  return hip_status(launch_fake_quantize(x, (int)x_dtype, M, K, ld_x, y, (int)y_dtype, ld_y, tensor_scale,
-                                         mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
+  return hip_status(launch_fake_quantize(x, (int)x_dtype, M, K, ld_x, block_size, y, (int)y_dtype, ld_y,
+                                         tensor_scale, mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
                                          static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
-                                int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
+nvfp4_status_t nvfp4_fake_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                   void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, float *tensor_scale,
+                                   nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
+  return nvfp4_fake_quantize_bs(x, x_dtype, M, K, ld_x, 16, y, y_dtype, ld_y, tensor_scale, mode, workspace,
+                                workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_dequantize_bs(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                   int64_t M, int64_t K, int block_size, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y,
+                                   void *stream) {
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
   nvfp4_status_t st = check_mk(M, K);
+  if (st != NVFP4_OK) return st;
+  st = check_bs(K, block_size);
   if (st != NVFP4_OK) return st;
   if (M == 0) return NVFP4_OK;  // empty: nothing to read or write
   if (!packed || !scales || !tensor_scale || !y) return NVFP4_ERR_NULL;
@@ -134,8 +163,13 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, co
     return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
-  return hip_status(
-      launch_dequantize(packed, scales, tensor_scale, M, K, y, (int)y_dtype, ld_y, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_dequantize(packed, scales, tensor_scale, M, K, block_size, y, (int)y_dtype, ld_y,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
+                                int64_t K, void *y, nvfp4_dtype_t y_dtype, int64_t ld_y, void *stream) {
+  return nvfp4_dequantize_bs(packed, scales, tensor_scale, M, K, 16, y, y_dtype, ld_y, stream);
 }
 
 size_t nvfp4_prepacked_bytes(int64_t N, int64_t K) {
@@ -144,28 +178,42 @@ size_t nvfp4_prepacked_bytes(int64_t N, int64_t K) {
   return (size_t)(Nu * Kc * (2048 + 256));
 }
 
-nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
-                                    void *prepacked, void *stream) {
+nvfp4_status_t nvfp4_prepack_weight_bs(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                                       int block_size, void *prepacked, void *stream) {
   nvfp4_status_t st = check_mk(N, K);
+  if (st != NVFP4_OK) return st;
+  st = check_bs(K, block_size);
   if (st != NVFP4_OK) return st;
   if (N == 0) return NVFP4_OK;  // empty weight
   if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
-  return hip_status(launch_prepack(packed, scales, N, K, prepacked, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_prepack(packed, scales, N, K, block_size, prepacked, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_prepack_weight(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                                    void *prepacked, void *stream) {
+  return nvfp4_prepack_weight_bs(packed, scales, N, K, 16, prepacked, stream);
+}
+
+nvfp4_status_t nvfp4_unpack_weight_bs(const void *prepacked, int64_t N, int64_t K, int block_size, uint8_t *packed,
+                                      uint8_t *scales, void *stream) {
+  nvfp4_status_t st = check_mk(N, K);
+  if (st != NVFP4_OK) return st;
+  st = check_bs(K, block_size);
+  if (st != NVFP4_OK) return st;
+  if (N == 0) return NVFP4_OK;  // empty weight
+  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
+  if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_unpack(prepacked, N, K, block_size, packed, scales, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
                                    void *stream) {
-  nvfp4_status_t st = check_mk(N, K);
-  if (st != NVFP4_OK) return st;
-  if (N == 0) return NVFP4_OK;  // empty weight
-  if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
-  if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
-  st = check_device();
-  if (st != NVFP4_OK) return st;
-  return hip_status(launch_unpack(prepacked, N, K, packed, scales, static_cast<hipStream_t>(stream)));
+  return nvfp4_unpack_weight_bs(prepacked, N, K, 16, packed, scales, stream);
 }
 
 size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
@@ -174,11 +222,13 @@ size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64
   return gemm_workspace_bytes((int)mode, M, N, K);
 }
 
-nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,
-                          const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
-                          int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                             const float *a_tensor_scale, int a_block_size, const void *b_prepacked,
+                             const float *b_tensor_scale, int64_t M, int64_t N, int64_t K, int64_t lda, void *c,
+                             nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace, size_t workspace_bytes,
+                             void *stream) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return NVFP4_ERR_MODE;
+  if (mode == NVFP4_W4A4 && check_bs(K, a_block_size) != NVFP4_OK) return NVFP4_ERR_SHAPE;
   if (mode == NVFP4_W4A16 && (a_scales || a_tensor_scale)) return NVFP4_ERR_NULL;
   if (!valid_dtype(c_dtype)) return NVFP4_ERR_DTYPE;
   if (N < 0) return NVFP4_ERR_SHAPE;
@@ -190,8 +240,8 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
   if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
   if (lda < K || ldc < N) return NVFP4_ERR_STRIDE;
   if (mode == NVFP4_W4A4) {
-    if ((lda % 16) != 0) return NVFP4_ERR_STRIDE;
-    if (!aligned(a, 8)) return NVFP4_ERR_ALIGN;
+    if ((lda % a_block_size) != 0) return NVFP4_ERR_STRIDE;  // whole scale blocks per row
+    if (!aligned(a, 8) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
   } else {
     if (!aligned(a, 16) || ((lda * 2) % 16) != 0) return NVFP4_ERR_ALIGN;
   }
@@ -214,11 +264,20 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
   g.N = N;
   g.K = K;
   g.lda = lda;
+  g.a_blk = (mode == NVFP4_W4A4) ? a_block_size : 16;
   g.c = c;
   g.out_dtype = (int)c_dtype;
   g.ldc = ldc;
   g.workspace = workspace;
   return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,
+                          const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
+                          int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return nvfp4_gemm_bs(mode, a, a_scales, a_tensor_scale, 16, b_prepacked, b_tensor_scale, M, N, K, lda, c, c_dtype,
+                       ldc, workspace, workspace_bytes, stream);
 }
 
 // ---- GEMM with NVFP4 output ------------------------------------------------------------------
@@ -229,12 +288,14 @@ size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t 
   return gemm_requant_workspace_bytes((int)mode, M, N, K);
 }
 
-nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
-                                  const float *a_tensor_scale, const void *b_prepacked, const float *b_tensor_scale,
-                                  int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,
-                                  const float *out_tensor_scale, uint8_t *out_packed, uint8_t *out_scales, float *y,
-                                  int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream) {
+nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                                     const float *a_tensor_scale, int a_block_size, const void *b_prepacked,
+                                     const float *b_tensor_scale, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                     const float *bias, nvfp4_act_t act, const float *out_tensor_scale,
+                                     uint8_t *out_packed, uint8_t *out_scales, float *y, int64_t ld_y, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return NVFP4_ERR_MODE;
+  if (mode == NVFP4_W4A4 && check_bs(K, a_block_size) != NVFP4_OK) return NVFP4_ERR_SHAPE;
   if (mode == NVFP4_W4A16 && (a_scales || a_tensor_scale)) return NVFP4_ERR_NULL;
   if (act != NVFP4_ACT_NONE && act != NVFP4_ACT_GELU_TANH) return NVFP4_ERR_MODE;
   if (N < 0 || (N % 16) != 0) return NVFP4_ERR_SHAPE;
@@ -248,8 +309,8 @@ nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_
   if (lda < K) return NVFP4_ERR_STRIDE;
   if (y && (ld_y < N || (ld_y % 4) != 0)) return NVFP4_ERR_STRIDE;
   if (mode == NVFP4_W4A4) {
-    if ((lda % 16) != 0) return NVFP4_ERR_STRIDE;
-    if (!aligned(a, 8)) return NVFP4_ERR_ALIGN;
+    if ((lda % a_block_size) != 0) return NVFP4_ERR_STRIDE;  // whole scale blocks per row
+    if (!aligned(a, 8) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
   } else {
     if (!aligned(a, 16) || ((lda * 2) % 16) != 0) return NVFP4_ERR_ALIGN;
   }
@@ -285,7 +346,18 @@ nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_
   g.qo.y = y;
   g.qo.ldy = ld_y;
   g.qo.act = (int)act;
+  g.a_blk = (mode == NVFP4_W4A4) ? a_block_size : 16;
   return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
+                                  const float *a_tensor_scale, const void *b_prepacked, const float *b_tensor_scale,
+                                  int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,
+                                  const float *out_tensor_scale, uint8_t *out_packed, uint8_t *out_scales, float *y,
+                                  int64_t ld_y, void *workspace, size_t workspace_bytes, void *stream) {
+  return nvfp4_gemm_requant_bs(mode, a, a_scales, a_tensor_scale, 16, b_prepacked, b_tensor_scale, M, N, K, lda, bias,
+                               act, out_tensor_scale, out_packed, out_scales, y, ld_y, workspace, workspace_bytes,
+                               stream);
 }
 
 // ---- MXFP4 ------------------------------------------------------------------------------------

@@ -6,16 +6,18 @@
 // MFMA step s uses its dword s), stored as two 16-byte parts so that a wave's 16-byte reads are
 // contiguous:
 //   codes   [N/32][K/128][part 2][lane 64][16 B]      2048 B per unit
-//   scales  [N/32][K/128][lane 64][4 B]               256 B per unit (blocks 4h..4h+3 of the lane)
+//   scales  [N/32][K/128][lane 64][4 B]               256 B per unit (16-k groups 4h..4h+3 of the lane)
 // with the scale region following the code region.  N pads to 32, K to 128, with zero codes and
-// zero scale bytes (zero scale makes padded k contribute exactly 0).
+// zero scale bytes (zero scale makes padded k contribute exactly 0).  A weight quantized with
+// BLK = 32 or 64 values per scale byte is expanded to one byte per 16 k (each byte repeated over
+// its block), so the GEMM reads the same layout whatever the weight's block size.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
 
 __global__ __launch_bounds__(256) void k_prepack(const uint8_t *__restrict__ packed, const uint8_t *__restrict__ scales,
-                                                 int64_t N, int64_t K, int64_t Kc, uint64_t nlanes,
+                                                 int64_t N, int64_t K, int blk, int64_t Kc, uint64_t nlanes,
                                                  uint8_t *__restrict__ out, uint64_t scale_region) {
   for (uint64_t t = blockIdx.x * 256ull + threadIdx.x; t < nlanes; t += gridDim.x * 256ull) {
     const uint64_t unit = t >> 6;
@@ -42,17 +44,17 @@ __global__ __launch_bounds__(256) void k_prepack(const uint8_t *__restrict__ pac
     uint32_t sw = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t blk = kc * 8 + 4 * h + j;
-      const uint32_t s = (n < N && blk < K / 16) ? scales[n * (K / 16) + blk] : 0u;
+      const int64_t k16 = (kc * 8 + 4 * h + j) * 16;  // first k of the lane's j-th 16-k group
+      const uint32_t s = (n < N && k16 < K) ? scales[n * (K / blk) + k16 / blk] : 0u;
       sw |= s << (8 * j);
     }
     *reinterpret_cast<uint32_t *>(out + scale_region + unit * 256 + (uint64_t)lane * 4) = sw;
   }
 }
 
-__global__ __launch_bounds__(256) void k_unpack(const uint8_t *__restrict__ in, int64_t N, int64_t K, int64_t Kc,
-                                                uint64_t nlanes, uint64_t scale_region, uint8_t *__restrict__ packed,
-                                                uint8_t *__restrict__ scales) {
+__global__ __launch_bounds__(256) void k_unpack(const uint8_t *__restrict__ in, int64_t N, int64_t K, int blk,
+                                                int64_t Kc, uint64_t nlanes, uint64_t scale_region,
+                                                uint8_t *__restrict__ packed, uint8_t *__restrict__ scales) {
   for (uint64_t t = blockIdx.x * 256ull + threadIdx.x; t < nlanes; t += gridDim.x * 256ull) {
     const uint64_t unit = t >> 6;
     const int lane = (int)(t & 63);
@@ -68,32 +70,33 @@ __global__ __launch_bounds__(256) void k_unpack(const uint8_t *__restrict__ in, 
     }
     const uint8_t *ss = in + scale_region + unit * 256 + (uint64_t)lane * 4;
     for (int j = 0; j < 4; ++j) {
-      const int64_t blk = kc * 8 + 4 * h + j;
-      if (blk < K / 16) scales[n * (K / 16) + blk] = ss[j];
+      const int64_t k16 = (kc * 8 + 4 * h + j) * 16;  // the first 16-k group of a block holds its byte
+      if (k16 < K && k16 % blk == 0) scales[n * (K / blk) + k16 / blk] = ss[j];
     }
   }
 }
 
-hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, void *out,
+hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, int blk, void *out,
                           hipStream_t stream) {
   const int64_t Nu = (N + 31) / 32, Kc = (K + 127) / 128;
   const uint64_t nlanes = (uint64_t)Nu * (uint64_t)Kc * 64ull;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
   uint64_t g = (nlanes + 255) / 256;
   if (g > 65536) g = 65536;
-  k_prepack<<<(unsigned)g, 256, 0, stream>>>(packed, scales, N, K, Kc, nlanes, static_cast<uint8_t *>(out),
+  k_prepack<<<(unsigned)g, 256, 0, stream>>>(packed, scales, N, K, blk, Kc, nlanes, static_cast<uint8_t *>(out),
                                              scale_region);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const void *in, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales, hipStream_t stream) {
+hipError_t launch_unpack(const void *in, int64_t N, int64_t K, int blk, uint8_t *packed, uint8_t *scales,
+                         hipStream_t stream) {
   const int64_t Nu = (N + 31) / 32, Kc = (K + 127) / 128;
   const uint64_t nlanes = (uint64_t)Nu * (uint64_t)Kc * 64ull;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
   uint64_t g = (nlanes + 255) / 256;
   if (g > 65536) g = 65536;
-  k_unpack<<<(unsigned)g, 256, 0, stream>>>(static_cast<const uint8_t *>(in), N, K, Kc, nlanes, scale_region, packed,
-                                            scales);
+  k_unpack<<<(unsigned)g, 256, 0, stream>>>(static_cast<const uint8_t *>(in), N, K, blk, Kc, nlanes, scale_region,
+                                            packed, scales);
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
 // YT < 0: write the NVFP4 tensor (packed codes + scale bytes).  YT = 0 / 1: fake quantization,
 // write dequantize(quantize(x)) as fp32 / bf16 into y [.][ld_y] instead (one pass, same values as
 // the two calls).
-template <int DT, bool DYNAMIC, bool DENSE, int YT>
+template <int DT, bool DYNAMIC, bool DENSE, int YT, int BLK>
 __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                                   FastDiv bpr, uint8_t *__restrict__ packed,
                                                   uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
                                                   void *__restrict__ y, int64_t ld_y) {
   using In = SegIn<DT>;
   constexpr int E = In::kElems;
-  using Map = Segments<E>;
+  using Map = Segments<E, BLK>;  // a block of BLK values spans Map::kLanesPerBlock adjacent lanes
   constexpr int U = kSegsPerLane;
   // the first tile's input loads are independent of S: issue them before the scale reduction
   const int lane = threadIdx.x & 63;
@@ -189,8 +189,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = fmaxf(amax, swap_lane1(amax));
-      if (Map::kLanesPerBlock == 4) amax = fmaxf(amax, swap_lane2(amax));
+      amax = group_max<Map::kLanesPerBlock>(amax);
       if (g >= nseg) continue;
       const uint32_t byte = block_byte(amax, qc);
       uint32_t codes;
@@ -221,54 +220,74 @@ static int grid_for(uint64_t nseg, int cap) {
   return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
 }
 
-template <int DT, bool DENSE, int YT>
-static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr, uint8_t *packed, uint8_t *scales,
-                         float *tensor_scale, bool dynamic, float *partial, void *y, int64_t ld_y,
+// bpr16 / bpr: blocks of 16 / of BLK values per row (the amax pass maps segments with 16-blocks)
+template <int DT, bool DENSE, int YT, int BLK>
+static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr16, FastDiv bpr, uint8_t *packed,
+                         uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, void *y, int64_t ld_y,
                          hipStream_t stream) {
   const int gq = grid_for(nseg, kQuantizeMaxGrid);
   if (dynamic) {
     const int ga = grid_for(nseg, kAmaxPartials);
-    k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr, partial);
-    k_quantize<DT, true, DENSE, YT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale, partial,
-                                                            ga, y, ld_y);
+    k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr16, partial);
+    k_quantize<DT, true, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
+                                                                 partial, ga, y, ld_y);
   } else {
-    k_quantize<DT, false, DENSE, YT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
-                                                             nullptr, 0, y, ld_y);
+    k_quantize<DT, false, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
+                                                                  nullptr, 0, y, ld_y);
+  }
+}
+
+template <int YT, int BLK>
+static void dispatch_dt(const void *x, int dtype, int64_t K, int64_t ld, uint64_t nseg, FastDiv bpr16,
+                        uint8_t *packed, uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, void *y,
+                        int64_t ld_y, hipStream_t stream) {
+  const FastDiv bpr = make_fastdiv((uint32_t)(K / BLK));
+  const bool dense = (ld == K) && (YT < 0 || ld_y == K);
+  if (dtype == 0) {
+    if (dense)
+      run_quantize<0, true, YT, BLK>(x, ld, nseg, bpr16, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y,
+                                     stream);
+    else
+      run_quantize<0, false, YT, BLK>(x, ld, nseg, bpr16, bpr, packed, scales, tensor_scale, dynamic, partial, y,
+                                      ld_y, stream);
+  } else {
+    if (dense)
+      run_quantize<1, true, YT, BLK>(x, ld, nseg, bpr16, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y,
+                                     stream);
+    else
+      run_quantize<1, false, YT, BLK>(x, ld, nseg, bpr16, bpr, packed, scales, tensor_scale, dynamic, partial, y,
+                                      ld_y, stream);
   }
 }
 
 template <int YT>
-static void dispatch_quantize(const void *x, int dtype, int64_t K, int64_t ld, uint64_t nseg, FastDiv bpr,
-                              uint8_t *packed, uint8_t *scales, float *tensor_scale, bool dynamic, float *partial,
-                              void *y, int64_t ld_y, hipStream_t stream) {
-  const bool dense = (ld == K) && (YT < 0 || ld_y == K);
-  if (dtype == 0) {
-    if (dense) run_quantize<0, true, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
-    else run_quantize<0, false, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
-  } else {
-    if (dense) run_quantize<1, true, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
-    else run_quantize<1, false, YT>(x, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
-  }
+static void dispatch_quantize(const void *x, int dtype, int64_t K, int64_t ld, int blk, uint8_t *packed,
+                              uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, void *y,
+                              int64_t ld_y, int64_t M, hipStream_t stream) {
+  const FastDiv bpr16 = make_fastdiv((uint32_t)(K / 16));
+  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
+  if (blk == 32)
+    dispatch_dt<YT, 32>(x, dtype, K, ld, nseg, bpr16, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
+  else if (blk == 64)
+    dispatch_dt<YT, 64>(x, dtype, K, ld, nseg, bpr16, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
+  else
+    dispatch_dt<YT, 16>(x, dtype, K, ld, nseg, bpr16, packed, scales, tensor_scale, dynamic, partial, y, ld_y, stream);
 }
 
-hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, uint8_t *packed,
+hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, uint8_t *packed,
                            uint8_t *scales, float *tensor_scale, bool dynamic, float *partial,
                            hipStream_t stream) {
-  const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
-  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
-  dispatch_quantize<-1>(x, dtype, K, ld, nseg, bpr, packed, scales, tensor_scale, dynamic, partial, nullptr, 0, stream);
+  dispatch_quantize<-1>(x, dtype, K, ld, blk, packed, scales, tensor_scale, dynamic, partial, nullptr, 0, M, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, void *y, int y_dtype,
-                                int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
+hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, void *y,
+                                int y_dtype, int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
                                 hipStream_t stream) {
-  const FastDiv bpr = make_fastdiv((uint32_t)(K / 16));
-  const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
   if (y_dtype == 0)
-    dispatch_quantize<0>(x, dtype, K, ld, nseg, bpr, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, stream);
+    dispatch_quantize<0>(x, dtype, K, ld, blk, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, M, stream);
   else
-    dispatch_quantize<1>(x, dtype, K, ld, nseg, bpr, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, stream);
+    dispatch_quantize<1>(x, dtype, K, ld, blk, nullptr, nullptr, tensor_scale, dynamic, partial, y, ld_y, M, stream);
   return hipGetLastError();
 }
 
