@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernel section")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 section")
     ap.add_argument("--no-requant", action="store_true", help="skip the fused-requantization section")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the 32/64-value block section")
     ap.add_argument("--kernel-probe", action="store_true",
                     help="only launch the dominant GEMM call and a 256 MiB device copy, --steps times each "
                          "(the workload of the rocprofv3 counter passes)")
@@ -215,6 +216,8 @@ def main():
         out["mxfp4"] = mxfp4_section(layers, side, stream, args.kernel_reps)
     if not args.no_requant:
         out["fused_requant"] = requant_section(layers, side, stream, args.kernel_reps)
+    if not args.no_blocks:
+        out["block_sizes"] = block_size_section(layers, side, stream, args.kernel_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
     print(json.dumps(out), flush=True)
@@ -455,6 +458,64 @@ def requant_section(layers, side, stream, reps):
     res["fc1_gemm_gelu_requant_us"] = round(time_graph([fc1_requant] * reps, side, stream), 2)
     res["mlp_unfused_us"] = round(time_graph([fc1_bf16, quant_dyn, lambda: fc2_from_h(hS)] * 4, side, stream) * 3, 2)
     res["mlp_fused_us"] = round(time_graph([fc1_requant, lambda: fc2_from_h(So)] * 4, side, stream) * 2, 2)
+    return res
+
+
+def block_size_section(layers, side, stream, reps):
+    """The step with 32 and 64 values per E4M3 scale byte (activations and weights alike): per linear,
+    the dynamic activation quantize and the W4A4 GEMM, each timed as back-to-back launches in one
+    graph; the step is their sum.  Also the dynamic quantize of a 32768 x 12288 bf16 N(0, 1) tensor
+    (generic S) at each block size, against HBM."""
+    import torch
+
+    import nvfp4_quantized_gemm_amd as nv
+
+    res = {}
+    for b in (32, 64):
+        r = {}
+        step_us = 0.0
+        flops_step = 0.0
+        for L in layers:
+            M, N, K = L["M"], L["N"], L["K"]
+            dev = L["x"].device
+            wp, ws, wS = nv.nvfp4_quantize(L["w_cpu"].to(dev), block_size=b)
+            bp = nv.nvfp4_prepack_weight(wp, ws)
+            del wp, ws
+            pa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            sa = torch.empty((M, K // b), dtype=torch.uint8, device=dev)
+            Sa = torch.empty(1, dtype=torch.float32, device=dev)
+            q_us = time_graph([lambda: nv.nvfp4_quantize(L["x"], Sa, static=False, packed=pa, scales=sa,
+                                                         workspace=L["qws"], block_size=b)] * reps, side, stream)
+            g_us = time_graph([lambda: nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bp, wS, N, K, torch.bfloat16,
+                                                     out=L["y"], workspace=L["gws"])] * reps, side, stream)
+            flops = 2.0 * M * N * K
+            r[L["name"]] = {"quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2),
+                            "gemm_TFLOPs": round(flops / (g_us * 1e-6) / 1e12, 1)}
+            step_us += q_us + g_us
+            flops_step += flops
+        r["block_step_us"] = round(step_us, 2)
+        r["block_TFLOPs"] = round(flops_step / (step_us * 1e-6) / 1e12, 1)
+        res[f"b{b}"] = r
+    torch.cuda.empty_cache()
+
+    M, K = 32768, 12288
+    dev = layers[0]["x"].device
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev)
+    packed = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    for b in (16, 32, 64):
+        scales = torch.empty((M, K // b), dtype=torch.uint8, device=dev)
+        us = time_graph([lambda: nv.nvfp4_quantize(x, S, static=False, packed=packed, scales=scales, workspace=qws,
+                                                   block_size=b)] * 10, side, stream)
+        nbytes = M * K * (2 + 2 + 0.5 + 1.0 / b)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"quantize_dynamic_bf16_{M}x{K}_generic_S_b{b}"] = {
+            "us": round(us, 2), "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+        del scales
+    del x, packed, qws
+    torch.cuda.empty_cache()
     return res
 
 
