@@ -160,11 +160,28 @@ struct Segments {
 template <int DT>
 struct SegIn;
 
+// NT: a streaming (non-temporal) load, for data that is read once: it keeps the caches for data
+// that is reused and streams markedly faster from HBM.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void *p) {
+  const u32x4 *q = static_cast<const u32x4 *>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(void *p, const u32x4 &v) {
+  u32x4 *q = static_cast<u32x4 *>(p);
+  if constexpr (NT) __builtin_nontemporal_store(v, q);
+  else *q = v;
+}
+
 template <>
 struct SegIn<0> {  // fp32: 4 values
   static constexpr int kElems = 4;
+  template <bool NT = false>
   __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem_off);
+    return load16<NT>(static_cast<const float *>(base) + elem_off);
   }
   __device__ static void unpack(const u32x4 &w, float v[4]) {
     v[0] = __uint_as_float(w.x);
@@ -177,8 +194,9 @@ struct SegIn<0> {  // fp32: 4 values
 template <>
 struct SegIn<1> {  // bf16: 8 values
   static constexpr int kElems = 8;
+  template <bool NT = false>
   __device__ static u32x4 raw(const void *base, uint64_t elem_off) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem_off);
+    return load16<NT>(static_cast<const uint16_t *>(base) + elem_off);
   }
   __device__ static void unpack(const u32x4 &w, float v[8]) {
     const uint32_t a[4] = {w.x, w.y, w.z, w.w};

@@ -13,6 +13,8 @@ namespace nvfp4 {
 
 namespace {
 constexpr int kSegsPerLane = 4;
+constexpr bool kCodesNT = true;  // code bytes are read once: streaming loads
+constexpr bool kOutNT = true;    // the output is written once: streaming stores
 }
 
 template <int OUT, bool DENSE, int BLK>
@@ -32,8 +34,12 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;
-      codes[u] = (E == 8) ? *reinterpret_cast<const uint32_t *>(packed + 4 * g)
-                          : (uint32_t) * reinterpret_cast<const uint16_t *>(packed + 2 * g);
+      if constexpr (kCodesNT)
+        codes[u] = (E == 8) ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(packed + 4 * g))
+                            : (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(packed + 2 * g));
+      else
+        codes[u] = (E == 8) ? *reinterpret_cast<const uint32_t *>(packed + 4 * g)
+                            : (uint32_t) * reinterpret_cast<const uint16_t *>(packed + 2 * g);
       sb[u] = scales[g >> Map::kShift];
     }
 #pragma unroll
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
         o.y = __float_as_uint(out[1]);
         o.z = __float_as_uint(out[2]);
         o.w = __float_as_uint(out[3]);
-        *reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off) = o;
+        store16<kOutNT>(static_cast<float *>(y) + off, o);
       } else {
         uint32_t p[4];
 #pragma unroll
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
         o.y = p[1];
         o.z = p[2];
         o.w = p[3];
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + off) = o;
+        store16<kOutNT>(static_cast<uint16_t *>(y) + off, o);
       }
     }
   }

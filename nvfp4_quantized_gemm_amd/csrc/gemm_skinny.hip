@@ -62,8 +62,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   };
   auto load_b = [&](int kc, BRegs &x) {
     const uint8_t *pc = bcode + (uint64_t)kc * 2048ull;
-    x.code[0] = *reinterpret_cast<const u32x4 *>(pc);
-    x.code[1] = *reinterpret_cast<const u32x4 *>(pc + 1024);
+    x.code[0] = load16<true>(pc);  // streaming: each weight byte is read once per call
+    x.code[1] = load16<true>(pc + 1024);
     x.sc = *reinterpret_cast<const uint32_t *>(bscale + (uint64_t)kc * 256ull);
   };
   auto load_a = [&](int kc, u32x4 *x) {

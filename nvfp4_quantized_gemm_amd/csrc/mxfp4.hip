@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const void *__restrict__ x,
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;
-      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
+      r[u] = In::template raw<true>(x, Map::template offset<DENSE>(g, bpr, ld));  // streaming: read once
     }
   };
   uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;
-      codes[u] = (E == 8) ? *reinterpret_cast<const uint32_t *>(packed + 4 * g)
-                          : (uint32_t) * reinterpret_cast<const uint16_t *>(packed + 2 * g);
+      codes[u] = (E == 8) ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(packed + 4 * g))
+                          : (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(packed + 2 * g));
       sb[u] = scales[g >> Map::kShift];
     }
 #pragma unroll
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
         o.y = __float_as_uint(out[1]);
         o.z = __float_as_uint(out[2]);
         o.w = __float_as_uint(out[3]);
-        *reinterpret_cast<u32x4 *>(static_cast<float *>(y) + off) = o;
+        store16<true>(static_cast<float *>(y) + off, o);  // streaming: written once
       } else {
         uint32_t p[4];
 #pragma unroll
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
         o.y = p[1];
         o.z = p[2];
         o.w = p[3];
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + off) = o;
+        store16<true>(static_cast<uint16_t *>(y) + off, o);
       }
     }
   }

@@ -11,7 +11,7 @@
 // 16-value block combine their maxima with cross-lane swaps, every lane derives the block's scale
 // byte and encodes its own values, lanes store their 4 (bf16) or 2 (fp32) code bytes contiguously
 // and the first lane of each block stores the scale byte.  Each lane keeps four segments' loads in
-// flight.  Dynamic mode runs k_amax first (same mapping, per-workgroup partial maxima, no atomics,
+// flight; the input is read with streaming (non-temporal) loads, its last use.  Dynamic mode runs k_amax first (same mapping, per-workgroup partial maxima, no atomics,
 // deterministic); every quantize workgroup reduces those partials itself and derives
 // S = RN32(amax / 2688).
 //
@@ -43,6 +43,13 @@
 namespace nvfp4 {
 
 constexpr int kSegsPerLane = 4;  // segments in flight per lane
+// Streaming (non-temporal) accesses: the input is read with them by both passes (faster from HBM,
+// also when the encode pass re-reads it); the NVFP4 output is stored normally so that the GEMM
+// that reads it next finds it in the caches; the fake-quantization output is streamed.
+constexpr bool kAmaxNT = true;
+constexpr bool kQuantNT = true;
+constexpr bool kOutNT = false;
+constexpr bool kFakeOutNT = true;
 
 // Fake quantization output: the lane's E codes dequantized exactly as the dequantize kernel does,
 // y = RN32((q * e) * S) with q * e exact, then bf16 (nearest, ties to even) for YT = 1.
@@ -68,7 +75,7 @@ __device__ __forceinline__ void store_fake(uint32_t codes, uint32_t byte, float 
     for (int h = 0; h < E / 4; ++h) {
       const u32x4 o = {__float_as_uint(out[4 * h]), __float_as_uint(out[4 * h + 1]), __float_as_uint(out[4 * h + 2]),
                        __float_as_uint(out[4 * h + 3])};
-      dst[h] = o;
+      store16<kFakeOutNT>(dst + h, o);
     }
   } else {
     uint32_t p[E / 2];
@@ -80,7 +87,7 @@ __device__ __forceinline__ void store_fake(uint32_t codes, uint32_t byte, float 
     uint16_t *dst = static_cast<uint16_t *>(y) + off;
     if (E == 8) {
       const u32x4 o = {p[0], p[1], p[2], p[3]};
-      *reinterpret_cast<u32x4 *>(dst) = o;
+      store16<kFakeOutNT>(dst, o);
     } else {
       const u32x2 o = {p[0], p[1]};
       *reinterpret_cast<u32x2 *>(dst) = o;
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;  // a repeated segment does not change the maximum
-      In::unpack(In::raw(x, Map::template offset<DENSE>(g, bpr, ld)), v[u]);
+      In::unpack(In::template raw<kAmaxNT>(x, Map::template offset<DENSE>(g, bpr, ld)), v[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;
-      r[u] = In::raw(x, Map::template offset<DENSE>(g, bpr, ld));
+      r[u] = In::template raw<kQuantNT>(x, Map::template offset<DENSE>(g, bpr, ld));
     }
   };
   uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
@@ -173,6 +180,40 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   const float S = s_S;
   const QuantConsts qc = make_quant_consts(S, DT == 1);
 
+  // encodes one segment (its E values already unpacked) as segment g
+  auto encode_seg = [&](const float (&v)[E], uint64_t g) {
+    // block maximum over the block's lanes (nseg is a multiple of the lanes per block, so a
+    // block's lanes are all in range or all out of range)
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max<Map::kLanesPerBlock>(amax);
+    if (g >= nseg) return;
+    const uint32_t byte = block_byte(amax, qc);
+    uint32_t codes;
+    if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
+      codes = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+    } else {
+      codes = encode_values<E>(v, byte, qc);
+    }
+    if (YT < 0) {
+      if constexpr (kOutNT) {
+        if (E == 8) __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(packed + 4 * g));
+        else __builtin_nontemporal_store((uint16_t)codes, reinterpret_cast<uint16_t *>(packed + 2 * g));
+        if ((lane & (Map::kLanesPerBlock - 1)) == 0)
+          __builtin_nontemporal_store((uint8_t)byte, scales + (g >> Map::kShift));
+      } else {
+        if (E == 8) *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
+        else *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
+        if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)byte;
+      }
+    } else {
+      store_fake<E, YT>(codes, byte, S, y, Map::template offset<DENSE>(g, bpr, ld_y));
+    }
+  };
+
   for (; t < ntiles; t += tstride) {
     // the next tile's loads are issued before this tile is encoded
     u32x4 cur[U];
@@ -181,32 +222,9 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
     if (t + tstride < ntiles) fetch(t + tstride, nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t g = t * (64 * U) + u * 64 + lane;
       float v[E];
       In::unpack(cur[u], v);
-      // block maximum over the block's lanes (nseg is a multiple of the lanes per block, so a
-      // block's lanes are all in range or all out of range)
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = group_max<Map::kLanesPerBlock>(amax);
-      if (g >= nseg) continue;
-      const uint32_t byte = block_byte(amax, qc);
-      uint32_t codes;
-      if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
-        codes = 0;
-#pragma unroll
-        for (int i = 0; i < E; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
-      } else {
-        codes = encode_values<E>(v, byte, qc);
-      }
-      if (YT < 0) {
-        if (E == 8) *reinterpret_cast<uint32_t *>(packed + 4 * g) = codes;
-        else *reinterpret_cast<uint16_t *>(packed + 2 * g) = (uint16_t)codes;
-        if ((lane & (Map::kLanesPerBlock - 1)) == 0) scales[g >> Map::kShift] = (uint8_t)byte;
-      } else {
-        store_fake<E, YT>(codes, byte, S, y, Map::template offset<DENSE>(g, bpr, ld_y));
-      }
+      encode_seg(v, t * (64 * U) + u * 64 + lane);
     }
   }
 }
