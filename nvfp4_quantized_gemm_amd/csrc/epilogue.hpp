@@ -24,7 +24,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int CW, int TM, int TN, typename OutT>
+template <int CW, int TM, int TN, typename OutT, bool NT = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float scale, OutT *__restrict__ C,
                                            int64_t ldc, int M, int N, int row0, int col0, bool vec,
                                            uint8_t *lds, int lane) {
@@ -63,7 +63,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
       const int row = row0 + i * 32 + r, col = col0 + cq;
       OutT *pc = C + (int64_t)row * ldc + col;
       if (vec && row < M && col + kEl <= N) {
-        *reinterpret_cast<u32x4 *>(pc) = v;
+        store16<NT>(pc, v);
       } else if (row < M && col < N) {
         // ragged edge: element by element (elements taken out of the registers by shifts, so the
         // staged vector never goes through memory)

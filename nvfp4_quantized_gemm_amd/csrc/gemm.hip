@@ -29,6 +29,9 @@
 namespace nvfp4 {
 
 constexpr int kChunk = 128;  // k per LDS stage
+constexpr bool kOutputNT = true;    // streaming stores for the bf16 / fp32 output
+constexpr bool kPartialNT = false;  // split-K partials (read back at once by the reduction)
+constexpr bool kReduceNT = false;   // the reduction reads the partials while they are still cached
 
 template <int MODE, int BM, int BN>
 struct TileCfg {
@@ -454,8 +457,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (splits > 1) {
     // unscaled fp32 partial tile -> partial[split][M][N]; the reduce kernel scales and converts
     const bool vec = (N % 4 == 0);  // 16-byte aligned rows; lanes check their own bounds
-    store_tile<BN / WN, TM, TN, float>(acc, 1.0f, partial + (int64_t)split * M * N, N, M, N, row0, col0, vec,
-                                       lds_wave, lane);
+    store_tile<BN / WN, TM, TN, float, kPartialNT>(acc, 1.0f, partial + (int64_t)split * M * N, N, M, N, row0, col0,
+                                                   vec, lds_wave, lane);
     return;
   }
   const float sab = (MODE == 0) ? (*a_ts) * (*b_ts) : *b_ts;
@@ -464,8 +467,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   } else {
     typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
     const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;  // 16-byte aligned rows
-    store_tile<BN / WN, TM, TN, OutT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec, lds_wave,
-                                      lane);
+    store_tile<BN / WN, TM, TN, OutT, kOutputNT>(acc, sab, static_cast<OutT *>(c), ldc, M, N, row0, col0, vec,
+                                                 lds_wave, lane);
   }
 }
 
@@ -543,14 +546,14 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
   const bool vec = (ldc % 4 == 0);  // 4-element stores stay aligned (c is 16-byte aligned)
   const int64_t nq = MN / 4;  // N % 4 == 0 here
   for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < nq; q += (int64_t)gridDim.x * 256) {
-    f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + 4 * q);
-    for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4 *>(partial + sp * MN + 4 * q);
+    f32x4 acc = __builtin_bit_cast(f32x4, load16<kReduceNT>(partial + 4 * q));
+    for (int sp = 1; sp < splits; ++sp) acc += __builtin_bit_cast(f32x4, load16<kReduceNT>(partial + sp * MN + 4 * q));
     const int64_t m = (4 * q) / N, n = (4 * q) % N;
     acc *= sab;
     if (OUT == 0) {
       float *dst = static_cast<float *>(c) + m * ldc + n;
       if (vec) {
-        *reinterpret_cast<f32x4 *>(dst) = acc;
+        store16<kOutputNT>(dst, __builtin_bit_cast(u32x4, acc));
       } else {
         dst[0] = acc.x;
         dst[1] = acc.y;
@@ -564,7 +567,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
         u32x2 o;
         o.x = __builtin_bit_cast(uint32_t, h0);
         o.y = __builtin_bit_cast(uint32_t, h1);
-        *reinterpret_cast<u32x2 *>(dst) = o;
+        if constexpr (kOutputNT) __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(dst));
+        else *reinterpret_cast<u32x2 *>(dst) = o;
       } else {
         dst[0] = (__bf16)acc.x;
         dst[1] = (__bf16)acc.y;

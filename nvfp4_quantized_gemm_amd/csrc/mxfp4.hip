@@ -360,8 +360,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   constexpr int CW = 256 / WN;  // columns per wave
   static_assert(W * 32 * EpiPitch<CW, 4>::kPitch <= S * Cfg::kStage, "epilogue staging fits the LDS ring");
   uint8_t *lds_wave = smem + wave * (32 * EpiPitch<CW, 4>::kPitch);
-  store_tile<CW, TM, TN, OutT>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * (256 / WM), n0 + wn * CW,
-                               vec, lds_wave, lane);
+  store_tile<CW, TM, TN, OutT, true>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * (256 / WM), n0 + wn * CW,
+                                     vec, lds_wave, lane);
 }
 
 // Generic fallback (any K % 32 == 0): one thread per output element.
