@@ -177,6 +177,9 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
  * A weight prepacked with any block size is read by every GEMM call the same way (its scales are
  * expanded to one byte per 16 k); a_block_size is the W4A4 activation's block size (lda must be a
  * multiple of it) and is ignored for W4A16.  nvfp4_gemm* also need a_scales 4-byte aligned.
+ * nvfp4_unpack_weight_bs inverts nvfp4_prepack_weight_bs of the same block size: it returns the
+ * byte stored for the first 16 k of each block, so unpacking with a block size other than the one
+ * the weight was prepacked with does not recover its scales.
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                  int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
