@@ -20,6 +20,7 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+T_START = time.perf_counter()
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
@@ -27,6 +28,11 @@ METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at DiT shapes; % of MFMA/HBM roofli
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (the block-scaled MXFP4 instruction)
+
+
+def progress(msg):
+    """One line per finished section on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg} ({time.perf_counter() - T_START:.1f} s)", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -212,18 +218,25 @@ def main():
         "breakdown": breakdown,
         "wall_s_timed": round(wall, 4),
     }
+    progress("block step timed")
     if not args.no_hbm:
         out["hbm_kernels"] = hbm_kernels(side, stream)
+        progress("bandwidth section done")
     if not args.no_mx:
         out["mxfp4"] = mxfp4_section(layers, side, stream, args.kernel_reps)
+        progress("MXFP4 section done")
     if not args.no_requant:
         out["fused_requant"] = requant_section(layers, side, stream, args.kernel_reps)
+        progress("fused-requantization section done")
     if not args.no_blocks:
         out["block_sizes"] = block_size_section(layers, side, stream, args.kernel_reps)
+        progress("block-size section done")
     if not args.no_other:
         out["other_configs"] = other_configs_section(side, stream, args.kernel_reps)
+        progress("video-DiT / weight-only section done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
+        progress("CPU oracle baseline done")
     print(json.dumps(out), flush=True)
 
 
