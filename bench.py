@@ -6,9 +6,12 @@ activation (amax pass + quantize pass) followed by the W4A4 GEMM with bf16 outpu
 quantized and prepacked once before timing (offline, as a deployed model ships them).  Inputs are
 seeded synthetic tensors resident in device memory before the timed region.
 
-The step's eight kernel launches are captured once in a HIP graph and replayed, so host launch
-overhead is not part of the measurement; every replay is checked bit-for-bit against an eager run
-first.  Prints one JSON line: `value` is the block's GEMM work (sum of 2 M N K) divided by the
+The step's 13 kernel launches (amax, encode and GEMM per linear, plus fc2's split-K reduction)
+are captured in a HIP graph, 10 steps per graph (the largest divisor of K up to 10), and the graph
+is replayed, so host launch overhead is not part of the measurement and each replay's own launch
+latency is paid once per 10 steps, as in a graph of a whole forward pass; the same K steps with
+one step per graph are reported beside the value.  Every replay is checked bit-for-bit against an
+eager run first.  Prints one JSON line: `value` is the block's GEMM work (sum of 2 M N K) divided by the
 measured step time (quantization included).  `roofline` describes the dominant GEMM launch, whose
 average duration is measured with HIP events around graph replays of back-to-back launches of that
 kernel on the stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
@@ -115,37 +118,54 @@ def main():
     torch.cuda.synchronize()
     eager = [L["y"].clone() for L in layers]
 
-    # ---- capture the step; check replays against the eager result -------------------------------
+    # ---- capture G steps per graph (G the largest divisor of K up to 10: each replay's launch
+    # latency is paid once per G steps, as in a graph of a whole forward pass); check replays
+    # against the eager result -----------------------------------------------------------------------
+    G = max(d for d in range(1, min(10, args.steps) + 1) if args.steps % d == 0)
     side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        for L in layers:
-            L["y"].zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        for L, ref in zip(layers, eager):
-            if not torch.equal(L["y"], ref):
-                raise RuntimeError(f"graph replay differs from eager result for {L['name']}")
 
-    # ---- timed region: K replays of the step ------------------------------------------------------
+    def capture(nsteps):
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(nsteps):
+                    step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for L in layers:
+                L["y"].zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for L, ref in zip(layers, eager):
+                if not torch.equal(L["y"], ref):
+                    raise RuntimeError(f"graph replay differs from eager result for {L['name']}")
+        return g
+
+    graph = capture(G)
+    graph1 = capture(1) if G > 1 else graph
+
+    # ---- timed region: K steps = K / G replays ------------------------------------------------------
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(args.steps // G):
         graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
+    # the same K steps with one step per graph (reported beside the value, not used for it)
+    t0.record(stream)
+    for _ in range(args.steps):
+        graph1.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_1 = t0.elapsed_time(t1) / args.steps
 
     # ---- per-kernel durations: graphs of back-to-back launches of one kernel -----------------------
     def kernel_us(fn, L):
@@ -209,7 +229,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "PixArt-style DiT block linears, W4A4, bf16 in/out", "M": 4096, "hidden": 1152,
                    "linears": {L["name"]: [L["K"], L["N"]] for L in layers}, "parallelism": "none (1 GPU)",
-                   "timing": "HIP-graph replay of the step"},
+                   "timing": f"HIP-graph replay, {G} steps per graph"},
+        "ms_per_step_one_step_per_graph": round(ms_step_1, 4),
         "roofline": roofline,
         "quantize": {"achieved_GBps": round(q_total_bytes / (q_total_us * 1e-6) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
                      "frac": round(q_total_bytes / (q_total_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
