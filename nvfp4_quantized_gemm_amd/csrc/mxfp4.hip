@@ -173,16 +173,21 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 // 256 x 256 tile per workgroup of WM x WN waves, each owning (256 / WM) x (256 / WN) = TM x TN
 // tiles of 32 x 32: 2 x 2 waves (one per SIMD, 128 x 128 each) or 2 x 4 waves (two per SIMD,
 // 128 x 64 each, so one wave's LDS and DMA waits overlap the other's MFMAs).  K in chunks of 128
-// (two 64-k MFMA steps).  LDS stage (36 KB):
-//   A codes  [16 blocks of 16 rows][4 pieces][16 rows][16 B]   A scales [8 row groups][64 lanes][4 B]
-//   B codes, B scales likewise (columns).
+// (two 64-k MFMA steps).  LDS stage (32 KB):
+//   A codes  [16 blocks of 16 rows][4 pieces][16 rows][16 B]   B codes likewise (columns).
 // A codes block holds 16 rows x the chunk's 64 bytes each, piece-major, so one DMA reads whole
 // 64-byte row segments and every 16-lane LDS read pass is contiguous; MFMA lane (r, h) of step s
-// reads piece 2 s + h of row r (k-half h of the step).  A scales word holds its row's 4 scale bytes
-// of the chunk (block 2 s + h of them feeds the MFMA: the lane shifts the word right by 8 h and
-// op_sel picks byte 2 s).  A 4-stage ring with
-// the DMA three chunks ahead and the next chunk's fragments read into registers during the current
-// chunk's MFMAs; one barrier per chunk.  Rows past M / N are clamped to the last one (never stored).
+// reads piece 2 s + h of row r (k-half h of the step).  A 4-stage ring with the DMA three chunks
+// ahead and the next chunk's fragments read into registers during the current chunk's MFMAs; one
+// barrier per chunk.
+// Scales come in blocks of 4 chunks, double-buffered beside the ring: a row's scale word of a
+// chunk (its 4 bytes, 4-byte aligned in the canonical [rows][K/32] layout) is one 4-byte
+// DMA lane, and one DMA covers 16 rows x 4 chunks (lane = 16 * chunk + row), so an operand's 256
+// rows take 16 DMAs per 4 chunks:  scale block [16 row blocks][4 chunks][16 rows][4 B].  Block
+// j + 1 is issued in the first chunk of block j, after that chunk's codes, and is needed from the
+// look-ahead read of chunk 4 j + 4 on (three chunks later); the chunk waits account for it.  Of a
+// word, block 2 s + h feeds the MFMA: the lane shifts the word right by 8 h and op_sel picks byte
+// 2 s.  Rows past M / N are clamped to the last one (never stored), chunks past K to the last.
 #ifndef MX_WM
 #define MX_WM 2
 #endif
@@ -219,14 +224,18 @@ template <int WM, int WN>
 struct MxCfg {
   static constexpr int kWaves = WM * WN;
   static constexpr int kTM = 8 / WM, kTN = 8 / WN;  // 32 x 32 tiles per wave
-  static constexpr int kCodes = 8 * 2 * 1024, kScales = 8 * 256;
-  static constexpr int kStage = 2 * (kCodes + kScales);
+  static constexpr int kCodes = 8 * 2 * 1024;       // one operand's codes of a chunk
+  static constexpr int kStage = 2 * kCodes;
   static constexpr int kStages = 4;
-  // DMA loads per wave per chunk, by kind (codes: 16 per operand, scales: 8 per operand)
-  static constexpr int kNC = 16 / kWaves, kNS = 8 / kWaves;
-  static constexpr int kSlots = 2 * (kNC + kNS);
-  static_assert(kNC * kWaves == 16 && kNS * kWaves == 8, "even DMA split");
-  static_assert(kStages * kStage <= 160 * 1024, "LDS ring fits");
+  static constexpr int kScaleBlk = 16 * 256;                    // one operand's scale words of 4 chunks
+  static constexpr int kScaleBase = kStages * kStage;           // [2 slots][A, B][kScaleBlk]
+  static constexpr int kLds = kScaleBase + 2 * 2 * kScaleBlk;
+  // DMA loads per wave: codes 16 per operand per chunk, scales 16 per operand per 4 chunks
+  static constexpr int kNC = 16 / kWaves, kNS = 16 / kWaves;
+  static constexpr int kSlots = 2 * kNC;   // per chunk
+  static constexpr int kSSlots = 2 * kNS;  // per scale block
+  static_assert(kNC * kWaves == 16 && kNS * kWaves == 16, "even DMA split");
+  static_assert(kLds <= 160 * 1024, "LDS fits");
 };
 }  // namespace
 
@@ -270,42 +279,52 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kNS; ++i) {
-    const int grp = wave + W * i;
-    oas[i] = (uint32_t)(min(m0 + 32 * grp + lr, M - 1) - m0) * srow;
-    obs[i] = (uint32_t)(min(n0 + 32 * grp + lr, N - 1) - n0) * srow;
+    // scale DMA d covers rows 16 d .. 16 d + 15: lane l takes row 16 d + l % 16, chunk l / 16 of the block
+    const int row16 = 16 * (wave + W * i) + (lane & 15);
+    oas[i] = (uint32_t)(min(m0 + row16, M - 1) - m0) * srow;
+    obs[i] = (uint32_t)(min(n0 + row16, N - 1) - n0) * srow;
   }
   auto issue = [&](int kc, int stage) {
     uint8_t *st = smem + stage * Cfg::kStage;
 #pragma unroll
     for (int i = 0; i < Cfg::kNC; ++i) g2l16(a_tile + (int64_t)kc * 64 + oa[i], st + (wave + W * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < Cfg::kNS; ++i) g2l4(as_tile + kc * 4 + oas[i], st + Cfg::kCodes + (wave + W * i) * 256);
-#pragma unroll
     for (int i = 0; i < Cfg::kNC; ++i)
-      g2l16(b_tile + (int64_t)kc * 64 + ob[i], st + Cfg::kCodes + Cfg::kScales + (wave + W * i) * 1024);
+      g2l16(b_tile + (int64_t)kc * 64 + ob[i], st + Cfg::kCodes + (wave + W * i) * 1024);
+  };
+  // scale block blk (chunks 4 blk .. 4 blk + 3, clamped to the last chunk) into slot blk % 2;
+  // 32-bit lane offsets on the wave-uniform tile bases
+  auto issue_scales = [&](int blk) {
+    const uint32_t kcw = (uint32_t)min(4 * blk + (lane >> 4), nk - 1) * 4u;
+    uint8_t *sl = smem + Cfg::kScaleBase + (blk & 1) * (2 * Cfg::kScaleBlk);
 #pragma unroll
-    for (int i = 0; i < Cfg::kNS; ++i)
-      g2l4(bs_tile + kc * 4 + obs[i], st + 2 * Cfg::kCodes + Cfg::kScales + (wave + W * i) * 256);
+    for (int i = 0; i < Cfg::kNS; ++i) g2l4(as_tile + (oas[i] + kcw), sl + (wave + W * i) * 256);
+#pragma unroll
+    for (int i = 0; i < Cfg::kNS; ++i) g2l4(bs_tile + (obs[i] + kcw), sl + Cfg::kScaleBlk + (wave + W * i) * 256);
   };
 
   u32x4 Af[2][TM][2], Bf[2][TN][2];
   uint32_t Sa[2][TM], Sb[2][TN];
-  auto read_frags = [&](int stage, int buf) {
+  // fragments and scale words of chunk kc (held in ring stage `stage`) into register buffer buf;
+  // row lr of row group grp has its word in scale row block 2 grp + lr / 16 at lane 16 (kc % 4) + lr % 16
+  auto read_frags = [&](int stage, int buf, int kc) {
     const uint8_t *st = smem + stage * Cfg::kStage;
+    const uint8_t *sc = smem + Cfg::kScaleBase + ((kc >> 2) & 1) * (2 * Cfg::kScaleBlk) +
+                        ((lane >> 4) & 1) * 256 + ((kc & 3) * 16 + (lane & 15)) * 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int grp = wm * TM + i;
 #pragma unroll
       for (int t = 0; t < 2; ++t) Af[buf][i][t] = *reinterpret_cast<const u32x4 *>(st + frag_off(grp, t, lane));
-      Sa[buf][i] = *reinterpret_cast<const uint32_t *>(st + Cfg::kCodes + grp * 256 + lane * 4);
+      Sa[buf][i] = *reinterpret_cast<const uint32_t *>(sc + grp * 512);
     }
-    const uint8_t *sb = st + Cfg::kCodes + Cfg::kScales;
+    const uint8_t *sb = st + Cfg::kCodes;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int grp = wn * TN + j;
 #pragma unroll
       for (int t = 0; t < 2; ++t) Bf[buf][j][t] = *reinterpret_cast<const u32x4 *>(sb + frag_off(grp, t, lane));
-      Sb[buf][j] = *reinterpret_cast<const uint32_t *>(sb + Cfg::kCodes + grp * 256 + lane * 4);
+      Sb[buf][j] = *reinterpret_cast<const uint32_t *>(sc + Cfg::kScaleBlk + grp * 512);
     }
   };
 
@@ -319,14 +338,21 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
 
   // Branch-free pipeline: near the end of K the DMA re-fetches the last chunk into the free stage
   // and the look-ahead reads a stale stage; neither result is used.
+  issue_scales(0);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(min(s, nk - 1), s);
-  wait_vmem_then_barrier<(S - 2) * Cfg::kSlots>();  // chunk 0 landed (later ones may be in flight)
-  read_frags(0, 0);
-  // one chunk; CUR (compile time) is the register buffer holding its fragments
+  wait_vmem_then_barrier<(S - 2) * Cfg::kSlots>();  // scale block 0 and chunk 0 landed
+  read_frags(0, 0, 0);
+  // one chunk; CUR (compile time) is the register buffer holding its fragments, P = kc % 4.  In
+  // issue order the DMAs are: chunk kc + 3's codes per chunk, and after them in phase 0 the scale
+  // block kc / 4 + 1.  "Chunk kc + 1 landed" therefore leaves one chunk's codes outstanding in
+  // phases 0 and 3 and also the scale block in phases 1 and 2; in phase 3 the scale block issued
+  // in phase 0 is thereby complete before the look-ahead reads chunk kc + 1 (its first chunk).
   auto chunk = [&](int kc, auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
-    wait_vmem_then_barrier<(S - 3) * Cfg::kSlots>();  // chunk kc+1 landed everywhere
+    const int P = kc & 3;  // wave-uniform: the branches below are scalar
+    if (P == 1 || P == 2) wait_vmem_then_barrier<(S - 3) * Cfg::kSlots + Cfg::kSSlots>();
+    else wait_vmem_then_barrier<(S - 3) * Cfg::kSlots>();
     // this chunk's scale words (read one chunk ago): lane (r, h) feeds blocks h and 2 + h, i.e.
     // bytes 0 and 2 after a shift by 8 h.  Done before the next reads are issued, so waiting for
     // the old reads does not wait for the new ones.
@@ -336,7 +362,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     for (int j = 0; j < TN; ++j) Sb[CUR][j] >>= 8 * lh;
     __builtin_amdgcn_sched_barrier(0);
     issue(min(kc + S - 1, nk - 1), (kc + S - 1) % S);   // into the stage chunk kc-1 used
-    read_frags((kc + 1) % S, CUR ^ 1);
+    if (P == 0) issue_scales(kc / 4 + 1);                 // into the slot block kc / 4 - 1 used
+    read_frags((kc + 1) % S, CUR ^ 1, kc + 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -424,7 +451,7 @@ static hipError_t launch_mx_tiled(const uint8_t *a, const uint8_t *as, const uin
                                   int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
   using Cfg = MxCfg<WM, WN>;
   const int tm = (int)((M + kMxTileM - 1) / kMxTileM), tn = (int)((N + kMxTileM - 1) / kMxTileM);
-  constexpr int smem = Cfg::kStages * Cfg::kStage;
+  constexpr int smem = Cfg::kLds;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, WM, WN>),
