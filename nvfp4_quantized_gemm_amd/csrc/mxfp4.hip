@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 // DMA lane, and one DMA covers 16 rows x 4 chunks (lane = 16 * chunk + row), so an operand's 256
 // rows take 16 DMAs per 4 chunks:  scale block [16 row blocks][4 chunks][16 rows][4 B].  Block
 // j + 1 is issued in the first chunk of block j, after that chunk's codes, and is needed from the
-// look-ahead read of chunk 4 j + 4 on (three chunks later); the chunk waits account for it.  Of a
+// look-ahead read of chunk 4 j + 4 on (three chunks later); the chunk waits account for it.  When
+// K % 512 == 0 and both scale arrays are 16-byte aligned, rows of scales are 16-byte aligned and a
+// row's 4 words of a block are one 16-byte DMA lane instead (SX = 4: 4 DMAs per operand per block,
+// block layout [256 rows][4 chunks][4 B]).  Of a
 // word, block 2 s + h feeds the MFMA: the lane shifts the word right by 8 h and op_sel picks byte
 // 2 s.  Rows past M / N are clamped to the last one (never stored), chunks past K to the last.
 #ifndef MX_WM
@@ -220,7 +223,7 @@ __device__ __forceinline__ int frag_off(int grp, int t, int lane) {
   return (2 * grp + (r >> 4)) * 1024 + (16 * (2 * t + h) + (r & 15)) * 16;
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int SX>
 struct MxCfg {
   static constexpr int kWaves = WM * WN;
   static constexpr int kTM = 8 / WM, kTN = 8 / WN;  // 32 x 32 tiles per wave
@@ -230,21 +233,23 @@ struct MxCfg {
   static constexpr int kScaleBlk = 16 * 256;                    // one operand's scale words of 4 chunks
   static constexpr int kScaleBase = kStages * kStage;           // [2 slots][A, B][kScaleBlk]
   static constexpr int kLds = kScaleBase + 2 * 2 * kScaleBlk;
-  // DMA loads per wave: codes 16 per operand per chunk, scales 16 per operand per 4 chunks
-  static constexpr int kNC = 16 / kWaves, kNS = 16 / kWaves;
-  static constexpr int kSlots = 2 * kNC;   // per chunk
-  static constexpr int kSSlots = 2 * kNS;  // per scale block
-  static_assert(kNC * kWaves == 16 && kNS * kWaves == 16, "even DMA split");
+  // DMA loads per wave: codes 16 per operand per chunk; scales per 4 chunks 16 per operand with one
+  // word per lane (SX = 1), or 4 per operand with a row's 4 words per lane (SX = 4)
+  static constexpr int kNC = 16 / kWaves, kNS = 16 / kWaves, kNS4 = 8 / kWaves;
+  static constexpr int kSlots = 2 * kNC;                       // per chunk
+  static constexpr int kSSlots = (SX == 1) ? 2 * kNS : kNS4;   // per scale block
+  static_assert(kNC * kWaves == 16 && kNS * kWaves == 16 && kNS4 * kWaves == 8, "even DMA split");
+  static_assert(SX == 1 || SX == 4, "scale words per DMA lane");
   static_assert(kLds <= 160 * 1024, "LDS fits");
 };
 }  // namespace
 
-template <int OUT, int WM, int WN>
+template <int OUT, int WM, int WN, int SX>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void k_mx_gemm(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ as, const uint8_t *__restrict__ b,
     const uint8_t *__restrict__ bs, int M, int N, int K, void *__restrict__ c, int64_t ldc, int tiles_m,
     int tiles_n) {
-  using Cfg = MxCfg<WM, WN>;
+  using Cfg = MxCfg<WM, WN, SX>;
   constexpr int TM = Cfg::kTM, TN = Cfg::kTN, S = Cfg::kStages, W = Cfg::kWaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -268,7 +273,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   // DMA sources: wave-uniform tile bases + 32-bit lane offsets (host: 256 * rowb < 2^31)
   const uint8_t *a_tile = a + (int64_t)m0 * rowb, *as_tile = as + (int64_t)m0 * srow;
   const uint8_t *b_tile = b + (int64_t)n0 * rowb, *bs_tile = bs + (int64_t)n0 * srow;
-  uint32_t oa[Cfg::kNC], ob[Cfg::kNC], oas[Cfg::kNS], obs[Cfg::kNS];
+  uint32_t oa[Cfg::kNC], ob[Cfg::kNC];
+  uint32_t oas[SX == 1 ? Cfg::kNS : 1], obs[SX == 1 ? Cfg::kNS : 1], osx[SX == 4 ? Cfg::kNS4 : 1];
 #pragma unroll
   for (int i = 0; i < Cfg::kNC; ++i) {
     // codes block d covers rows 16 d .. 16 d + 15 with all 64 bytes of each: lane l takes row
@@ -277,12 +283,22 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
     oa[i] = (uint32_t)(min(m0 + row16, M - 1) - m0) * rowb + 16 * piece;
     ob[i] = (uint32_t)(min(n0 + row16, N - 1) - n0) * rowb + 16 * piece;
   }
+  if constexpr (SX == 1) {
 #pragma unroll
-  for (int i = 0; i < Cfg::kNS; ++i) {
-    // scale DMA d covers rows 16 d .. 16 d + 15: lane l takes row 16 d + l % 16, chunk l / 16 of the block
-    const int row16 = 16 * (wave + W * i) + (lane & 15);
-    oas[i] = (uint32_t)(min(m0 + row16, M - 1) - m0) * srow;
-    obs[i] = (uint32_t)(min(n0 + row16, N - 1) - n0) * srow;
+    for (int i = 0; i < Cfg::kNS; ++i) {
+      // scale DMA d covers rows 16 d .. 16 d + 15: lane l takes row 16 d + l % 16, chunk l / 16 of the block
+      const int row16 = 16 * (wave + W * i) + (lane & 15);
+      oas[i] = (uint32_t)(min(m0 + row16, M - 1) - m0) * srow;
+      obs[i] = (uint32_t)(min(n0 + row16, N - 1) - n0) * srow;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cfg::kNS4; ++i) {
+      // scale DMA q (0..7) covers operand q / 4, rows 64 (q % 4) .. + 63, one row per lane
+      const int q = wave + W * i, row64 = 64 * (q & 3) + lane;
+      osx[i] = (q >> 2) ? (uint32_t)(min(n0 + row64, N - 1) - n0) * srow
+                        : (uint32_t)(min(m0 + row64, M - 1) - m0) * srow;
+    }
   }
   auto issue = [&](int kc, int stage) {
     uint8_t *st = smem + stage * Cfg::kStage;
@@ -295,12 +311,22 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   // scale block blk (chunks 4 blk .. 4 blk + 3, clamped to the last chunk) into slot blk % 2;
   // 32-bit lane offsets on the wave-uniform tile bases
   auto issue_scales = [&](int blk) {
-    const uint32_t kcw = (uint32_t)min(4 * blk + (lane >> 4), nk - 1) * 4u;
     uint8_t *sl = smem + Cfg::kScaleBase + (blk & 1) * (2 * Cfg::kScaleBlk);
+    if constexpr (SX == 1) {
+      const uint32_t kcw = (uint32_t)min(4 * blk + (lane >> 4), nk - 1) * 4u;
 #pragma unroll
-    for (int i = 0; i < Cfg::kNS; ++i) g2l4(as_tile + (oas[i] + kcw), sl + (wave + W * i) * 256);
+      for (int i = 0; i < Cfg::kNS; ++i) g2l4(as_tile + (oas[i] + kcw), sl + (wave + W * i) * 256);
 #pragma unroll
-    for (int i = 0; i < Cfg::kNS; ++i) g2l4(bs_tile + (obs[i] + kcw), sl + Cfg::kScaleBlk + (wave + W * i) * 256);
+      for (int i = 0; i < Cfg::kNS; ++i) g2l4(bs_tile + (obs[i] + kcw), sl + Cfg::kScaleBlk + (wave + W * i) * 256);
+    } else {
+      // nk % 4 == 0 here: blocks are whole; the look-ahead past the last block re-reads the last
+      const uint32_t kcw = (uint32_t)min(blk, nk / 4 - 1) * 16u;
+#pragma unroll
+      for (int i = 0; i < Cfg::kNS4; ++i) {
+        const int q = wave + W * i;
+        g2l16(((q >> 2) ? bs_tile : as_tile) + (osx[i] + kcw), sl + (q >> 2) * Cfg::kScaleBlk + (q & 3) * 1024);
+      }
+    }
   };
 
   u32x4 Af[2][TM][2], Bf[2][TN][2];
@@ -309,8 +335,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   // row lr of row group grp has its word in scale row block 2 grp + lr / 16 at lane 16 (kc % 4) + lr % 16
   auto read_frags = [&](int stage, int buf, int kc) {
     const uint8_t *st = smem + stage * Cfg::kStage;
+    // SX = 1: row lr's word at row block 2 grp + lr / 16, lane 16 (kc % 4) + lr % 16;
+    // SX = 4: at row 32 grp + lr, word kc % 4 (16 bytes per row)
     const uint8_t *sc = smem + Cfg::kScaleBase + ((kc >> 2) & 1) * (2 * Cfg::kScaleBlk) +
-                        ((lane >> 4) & 1) * 256 + ((kc & 3) * 16 + (lane & 15)) * 4;
+                        ((SX == 1) ? ((lane >> 4) & 1) * 256 + ((kc & 3) * 16 + (lane & 15)) * 4
+                                   : (lane & 31) * 16 + (kc & 3) * 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int grp = wm * TM + i;
@@ -446,21 +475,21 @@ hipError_t launch_mx_dequantize(const uint8_t *packed, const uint8_t *scales, in
   return hipGetLastError();
 }
 
-template <int OUT, int WM, int WN>
+template <int OUT, int WM, int WN, int SX>
 static hipError_t launch_mx_tiled(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
                                   int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
-  using Cfg = MxCfg<WM, WN>;
+  using Cfg = MxCfg<WM, WN, SX>;
   const int tm = (int)((M + kMxTileM - 1) / kMxTileM), tn = (int)((N + kMxTileM - 1) / kMxTileM);
   constexpr int smem = Cfg::kLds;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, WM, WN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, WM, WN, SX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_mx_gemm<OUT, WM, WN><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c, ldc, tm,
-                                                                     tn);
+  k_mx_gemm<OUT, WM, WN, SX><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c,
+                                                                         ldc, tm, tn);
   return hipGetLastError();
 }
 
@@ -473,7 +502,11 @@ static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const 
     k_mx_gemm_generic<OUT><<<(unsigned)grid, 256, 0, stream>>>(a, as, b, bs, M, N, K, c, ldc);
     return hipGetLastError();
   }
-  return launch_mx_tiled<OUT, MX_WM, MX_WN>(a, as, b, bs, M, N, K, c, ldc, stream);
+  // a row's 4 scale words of a 4-chunk block are one 16-byte DMA lane when rows (K / 32 bytes)
+  // and both scale arrays are 16-byte aligned
+  const bool sx4 = K % 512 == 0 && reinterpret_cast<uintptr_t>(as) % 16 == 0 && reinterpret_cast<uintptr_t>(bs) % 16 == 0;
+  if (sx4) return launch_mx_tiled<OUT, MX_WM, MX_WN, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
+  return launch_mx_tiled<OUT, MX_WM, MX_WN, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
 }
 
 hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,

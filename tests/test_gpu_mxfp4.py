@@ -89,12 +89,23 @@ def test_mx_dequantize_exact(out_dtype, ld):
         assert (out[:, K:] == 3.0).all()
 
 
-def run_mx_gemm(x_cpu, w_cpu, out_dtype, sample=None):
+def at_offset(t, off):
+    """A copy of t whose data starts `off` bytes into a fresh allocation (alignment control)."""
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def run_mx_gemm(x_cpu, w_cpu, out_dtype, sample=None, scale_offset=0):
     M, K = x_cpu.shape
     N = w_cpu.shape[0]
-    say(f"[mx gemm] M={M} N={N} K={K} out={out_dtype} sample={sample}")
+    say(f"[mx gemm] M={M} N={N} K={K} out={out_dtype} sample={sample} scale offset={scale_offset}")
     a, as_ = nv.nvfp4_mx_quantize(x_cpu.to(DEV))
     b, bs = nv.nvfp4_mx_quantize(w_cpu.to(DEV))
+    if scale_offset:
+        as_, bs = at_offset(as_, scale_offset), at_offset(bs, scale_offset)
+        assert as_.data_ptr() % 16 == scale_offset % 16
     pad = 8
     buf = torch.full((M, N + pad), 5.0, dtype=out_dtype, device=DEV)
     y = buf[:, :N]
@@ -128,12 +139,23 @@ def test_mx_gemm_tiny_full():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 32, 128), (17, 33, 160), (300, 520, 256), (255, 100, 1152),
-                                   (1000, 1000, 1280), (64, 64, 32), (513, 257, 384)])
+                                   (1000, 1000, 1280), (64, 64, 32), (513, 257, 384),
+                                   (300, 520, 1024), (513, 257, 2048)])
 def test_mx_gemm_ragged(M, N, K):
+    """K % 512 == 0 (with 16-byte aligned scales) takes the 16-byte scale-block loads, the other K
+    the 4-byte ones."""
     g = torch.Generator().manual_seed(M + 3 * N + 7 * K)
     x = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
     run_mx_gemm(x, w, torch.float32)
+
+
+def test_mx_gemm_scales_4_byte_aligned():
+    """Scale arrays that are 4- but not 16-byte aligned with K % 512 == 0: the 4-byte scale loads."""
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(300, 2048, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(520, 2048, generator=g)).to(torch.bfloat16)
+    run_mx_gemm(x, w, torch.float32, scale_offset=4)
 
 
 def test_mx_gemm_dit_shapes_sampled():
