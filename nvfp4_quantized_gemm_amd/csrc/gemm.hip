@@ -29,20 +29,21 @@
 namespace nvfp4 {
 
 constexpr int kChunk = 128;  // k per LDS stage
+constexpr int64_t kW4A16TallM = 512;  // W4A16 rows from which 256-row tiles are used
 constexpr bool kOutputNT = true;    // streaming stores for the bf16 / fp32 output
 constexpr bool kPartialNT = false;  // split-K partials (read back at once by the reduction)
 constexpr bool kReduceNT = false;   // the reduction reads the partials while they are still cached
 
 template <int MODE, int BM, int BN>
 struct TileCfg {
-  static constexpr int kALds = (MODE == 0) ? BM * 64 : BM * 256;  // codes or bf16
+  // W4A16 with 256-row tiles stages half chunks (64 k, one part of the prepacked units): a whole
+  // chunk of bf16 A rows (64 KB) would leave room for only two stages
+  static constexpr bool kHalf = (MODE == 1 && BM == 256);
+  static constexpr int kALds = (MODE == 0) ? BM * 64 : (kHalf ? BM * 128 : BM * 256);  // codes or bf16
   static constexpr int kASLds = (MODE == 0) ? BM * 8 : 0;
-  static constexpr int kBLds = BN * 64;
+  static constexpr int kBLds = kHalf ? BN * 32 : BN * 64;
   static constexpr int kBSLds = BN * 8;
   static constexpr int kStage = kALds + kASLds + kBLds + kBSLds;
-  static constexpr int kAIters = (MODE == 0) ? (BM * 4) / 256 : (BM * 16) / 256;  // 16-B loads per thread
-  static constexpr int kBIters = (BN * 128) / (32 * 256);                          // BN/32 units x 128 chunks
-  static constexpr int kBSChunks = BN / 2;                                          // 16-B chunks of B scales
 };
 
 // exact E2M1 decode of the 8 codes of a dword (element 2j in the low nibble of byte j)
@@ -104,9 +105,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using Cfg = TileCfg<MODE, BM, BN>;
   constexpr int TM = BM / WM / 32;  // MFMA tiles per wave along M
   constexpr int TN = BN / WN / 32;
-  constexpr int NA = (MODE == 0) ? (BM / 32) * 2 : (BM / 32) * 8;  // 1-KB A blocks per stage
-  constexpr int NAS = (MODE == 0) ? BM / 32 : 0;                    // 256-B A scale blocks
-  constexpr int NB = (BN / 32) * 2, NBS = BN / 32;
+  constexpr bool HALF = Cfg::kHalf;
+  constexpr int NA = (MODE == 0) ? (BM / 32) * 2 : (BM / 32) * (HALF ? 4 : 8);  // 1-KB A blocks per stage
+  constexpr int NAS = (MODE == 0) ? BM / 32 : 0;                                 // 256-B A scale blocks
+  constexpr int NB = (BN / 32) * (HALF ? 1 : 2), NBS = BN / 32;
   static_assert(NA % 4 == 0 && NB % 4 == 0 && NBS % 4 == 0 && NAS % 4 == 0, "block counts");
   static_assert(4 * 32 * EpiPitch<BN / WN, 4>::kPitch <= 3 * Cfg::kStage, "epilogue staging fits the LDS ring");
   constexpr int kAStep = (MODE == 0) ? 64 : 256;  // A bytes per row per chunk
@@ -156,7 +158,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int row = min(m0 + sub * 32 + lr, M - 1) - m0;
       oa[i] = (uint32_t)(row * (uint32_t)arow_bytes) + 32 * lh + 16 * part;
     } else {
-      const int sub = q >> 3, st = q & 7;
+      // lane (r, h) of step st holds A[row r][k = 64 h + 8 st .. + 8) of the chunk (as B's lanes);
+      // a half-chunk stage holds steps 4 p .. 4 p + 3 of part p (its offset 64 p bytes added at issue)
+      const int sub = HALF ? q >> 2 : q >> 3, st = HALF ? q & 3 : q & 7;
       const int row = min(m0 + sub * 32 + lr, M - 1) - m0;
       oa[i] = (uint32_t)(row * (uint32_t)arow_bytes) + 2 * (64 * lh + 8 * st);
     }
@@ -177,10 +181,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return ((uint64_t)nu * (uint64_t)Kc + (uint64_t)kc);
   };
 
+  // kc: the chunk; HALF: kc is the half-chunk stage g (chunk g / 2, part g % 2)
   auto issue_slot = [&](int kc, int buf, int t) {
     uint8_t *st = smem + buf * Cfg::kStage;
+    const int part = HALF ? (kc & 1) : 0;
+    if (HALF) kc >>= 1;
     if (t < NA / 4) {
-      g2l16(a_tile + (int64_t)kc * kAStep + oa[t], st + (wave + 4 * t) * 1024);
+      g2l16(a_tile + (int64_t)kc * kAStep + 64 * part + oa[t], st + (wave + 4 * t) * 1024);
     } else if (t < NA / 4 + NAS / 4) {
       const int i = t - NA / 4;
       if constexpr (ABLK == 64)
@@ -189,8 +196,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         g2l4(as_tile + kc * (128 / ABLK) + oas[i], st + Cfg::kALds + (wave + 4 * i) * 256);
     } else if (t < NA / 4 + NAS / 4 + NB / 4) {
       const int i = t - NA / 4 - NAS / 4, q = wave + 4 * i;
-      g2l16(bp + b_unit(q >> 1, kc) * 2048ull + (q & 1) * 1024 + ob,
-            st + Cfg::kALds + Cfg::kASLds + q * 1024);
+      if (HALF)
+        g2l16(bp + b_unit(q, kc) * 2048ull + part * 1024 + ob, st + Cfg::kALds + Cfg::kASLds + q * 1024);
+      else
+        g2l16(bp + b_unit(q >> 1, kc) * 2048ull + (q & 1) * 1024 + ob, st + Cfg::kALds + Cfg::kASLds + q * 1024);
     } else {
       const int i = t - NA / 4 - NAS / 4 - NB / 4, q = wave + 4 * i;
       g2l4(bp + scale_region + b_unit(q, kc) * 256ull + obs, st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + q * 256);
@@ -382,18 +391,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     chunk(0, std::true_type{});
     for (int kc = 1; kc < nk; ++kc) chunk(kc, std::false_type{});
+  } else if constexpr (HALF) {
+    // ---- W4A16, 256-row tiles: half-chunk stages (part p of each chunk: its 4 MFMA steps); per
+    // stage the wave's B codes and scales into registers, the DMA of stage g + 2 into the third
+    // buffer, then 4 steps with the next step's B dequantization and A reads pipelined beside the
+    // current step's MFMAs.  Each dequantized B fragment feeds TM = 8 MFMAs. ----
+    const int ng = 2 * (kend - kbeg);
+    issue(2 * kbeg, 0);
+    if (ng > 1) {
+      issue(2 * kbeg + 1, 1);
+      wait_vmem_then_barrier<NSLOT>();
+    } else {
+      wait_vmem_then_barrier<0>();
+    }
+    for (int g = 0; g < ng; ++g) {
+      const int cur = g % 3;
+      if (g > 0) {
+        if (g + 1 < ng) wait_vmem_then_barrier<NSLOT>();  // stage g + 1's DMA may be outstanding
+        else wait_vmem_then_barrier<0>();
+      }
+      const uint8_t *st = smem + cur * Cfg::kStage;
+      const uint8_t *sA = st, *sB = st + Cfg::kALds, *sBS = sB + Cfg::kBLds;
+      u32x4 bc[TN];
+      uint32_t bsw[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int unit = wn * (BN / WN / 32) + j;
+        bsw[j] = *reinterpret_cast<const uint32_t *>(sBS + (unit * 64 + lane) * 4);
+        bc[j] = *reinterpret_cast<const u32x4 *>(sB + (unit * 64 + lane) * 16);
+      }
+      if (g + 2 < ng) issue(2 * kbeg + g + 2, (g + 2) % 3);
+      // part p's steps 4 p + q use the lane's 16-k blocks 2 p + q / 2 (scale bytes 2 p, 2 p + 1)
+      const int p = g & 1;
+      float eb[TN][2];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) eb[j][t] = e4m3_to_f32((bsw[j] >> (16 * p + 8 * t)) & 0xffu);
+      bf16x8 bf[2][TN];
+      u32x4 ar[2][TM];
+      auto deq = [&](int q, int slot) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[slot][j] = dequant_bf16x8(bc[j][q], eb[j][q >> 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int sub = wm * (BM / WM / 32) + i;
+          ar[slot][i] = *reinterpret_cast<const u32x4 *>(sA + ((sub * 4 + q) * 64 + lane) * 16);
+        }
+      };
+      deq(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int slot = q & 1;
+        if (q + 1 < 4) deq(q + 1, slot ^ 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const bf16x8 afr = __builtin_bit_cast(bf16x8, ar[slot][i]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[slot][j], afr, acc[i][j], 0, 0, 0);
+        }
+        if (q + 1 < 4) {
+#pragma unroll
+          for (int t = 0; t < TM * TN; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (18 * TN) / (TM * TN) + 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   } else {
     // ---- W4A16: chunk fragments into registers, next chunk's DMA, 8 pipelined steps ----
+    // The DMA of chunk kc + 2 is issued during chunk kc into the third stage; a chunk waits only for
+    // its own DMA (the next chunk's may still be in flight), so the loads have two chunks to land.
     const int nk = kend - kbeg;
     issue(kbeg, 0);
-    if (nk > 1) issue(kbeg + 1, 1);
-    wait_vmem();
-    __syncthreads();
+    if (nk > 1) {
+      issue(kbeg + 1, 1);
+      wait_vmem_then_barrier<NSLOT>();
+    } else {
+      wait_vmem_then_barrier<0>();
+    }
     for (int kc = 0; kc < nk; ++kc) {
       const int cur = kc % 3;
       if (kc > 0) {
-        wait_vmem();
-        __syncthreads();
+        if (kc + 1 < nk) wait_vmem_then_barrier<NSLOT>();  // chunk kc + 1's DMA may be outstanding
+        else wait_vmem_then_barrier<0>();                 // nothing was issued after chunk kc
       }
       const uint8_t *st = smem + cur * Cfg::kStage;
       const uint8_t *sA = st, *sB = st + Cfg::kALds + Cfg::kASLds, *sBS = sB + Cfg::kBLds;
@@ -652,8 +737,11 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
       pl.waves = per >= 48 ? 16 : (per >= 16 ? 8 : 4);
       return pl;
     }
-    pl.variant = GemmVariant::W4A16_128x256;
-    const int64_t tb = ((M + 127) / 128) * ((N + 255) / 256);
+    // 256-row tiles reuse each dequantized B fragment for 8 MFMAs instead of 4 (B dequantization
+    // is the loop's VALU work); 128-row tiles keep small M from padding a 256-row tile
+    const bool tall = M >= kW4A16TallM;
+    pl.variant = tall ? GemmVariant::W4A16_256x256 : GemmVariant::W4A16_128x256;
+    const int64_t tb = ((M + (tall ? 255 : 127)) / (tall ? 256 : 128)) * ((N + 255) / 256);
     int best = 1;
     for (int sp = 2; sp <= 16; ++sp)
       if (tb * sp <= cus && Kc / sp >= 6 && N % 4 == 0) best = sp;
@@ -723,6 +811,15 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
       }
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
+    case GemmVariant::W4A16_256x256: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<1, 256, 256, 1, 4, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
+      }
+      return launch_tiled<1, 256, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A16_Skinny:
       return launch_gemm_skinny(g, pl.waves, pl.splits, static_cast<float *>(g.workspace), stream);

@@ -25,7 +25,7 @@ hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t 
 hipError_t launch_unpack(const void *in, int64_t N, int64_t K, int blk, uint8_t *packed, uint8_t *scales,
                          hipStream_t stream);
 
-enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256, W4A16_Skinny };
+enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A16_128x256, W4A16_256x256, W4A16_Skinny };
 
 struct GemmPlan {
   GemmVariant variant = GemmVariant::Generic;

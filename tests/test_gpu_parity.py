@@ -343,7 +343,9 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
                                    # streaming kernel (M <= 32): K split over workgroups, ragged last unit
                                    (1, 1000, 2048), (31, 1000, 2048), (7, 98, 1536), (16, 4096, 3072), (3, 200, 4096),
                                    # tiled kernel with K split
-                                   (200, 520, 2048)])
+                                   (200, 520, 2048),
+                                   # 256-row tiles (half-chunk stages): ragged M and N, K split, 9 chunks
+                                   (600, 520, 384), (512, 256, 4096), (1000, 300, 1152)])
 def test_gemm_w4a16_ragged(M, N, K):
     g = torch.Generator().manual_seed(M * 5 + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
