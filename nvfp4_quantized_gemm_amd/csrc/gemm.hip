@@ -84,15 +84,16 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 
 // MODE 0 = W4A4 (fp16 MFMA), 1 = W4A16 (bf16 MFMA).  WM x WN waves of (BM/WM) x (BN/WN).
 //
-// LDS stage layout (one per buffer, two buffers):
+// LDS: a ring of three stages, the DMA two stages ahead of the MFMAs.  Stage layout:
 //   A codes   [BM/32][2 parts][64 lanes][16 B]   (MODE 0)  or  A bf16 [BM/32][8 steps][64 lanes][16 B]
 //   A scales  [BM/32][64 lanes][4 B]             (MODE 0)
 //   B codes   [BN/32][2 parts][64 lanes][16 B]   B scales [BN/32][64 lanes][4 B]
+// A stage is one 128-k chunk, except for W4A16 with 256-row tiles, whose stages are half chunks
+// (part p: A bf16 [BM/32][4 steps][64 lanes][16 B], B codes [BN/32][64 lanes][16 B]).
 // Each 1-KB (or 256-B) block is filled by one wave-wide LDS-DMA load whose lane addresses implement
 // the row-major -> lane-order permutation for A; B is prepacked in exactly this order.  Rows past
-// M and columns past N are clamped to the last valid one (their results are never stored).
-// Per chunk a wave first reads all of its fragments for the chunk into registers, then issues the
-// next chunk's loads into the other buffer, then runs its 8 MFMA steps from registers.
+// M and columns past N are clamped to the last valid one (their results are never stored).  The
+// W4A4 loop and the two W4A16 loops below describe their own register pipelines.
 // ABLK: values per A scale byte along K (16, 32 or 64; W4A4).  Lane l = r + 32 h needs the bytes of
 // the blocks under its 64 k of a chunk: 4, 2 or 1 bytes, fetched as the aligned dword holding them
 // and shifted into place when read.
