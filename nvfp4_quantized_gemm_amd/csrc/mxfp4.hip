@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int lr = lane & 31, lh = lane >> 5;
+  const int lh = lane >> 5;
 
   // XCD-aware grouped tile order (bijective on the multiple-of-8 prefix), as in the NVFP4 GEMM
   const int ntiles = tiles_m * tiles_n;
