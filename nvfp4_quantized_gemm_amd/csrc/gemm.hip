@@ -271,7 +271,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int unit = wn * (BN / WN / 32) + j;
-        Sb[j] = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (unit * 64 + lane) * 4);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (unit * 64 + lane) * 4);
+        // units past N hold a clamped copy of the last unit and their results are never stored:
+        // zero scales make their operands zero, which draws less power in the matrix cores
+        Sb[j] = (n0 / 32 + unit < Nu) ? w : 0u;
       }
     };
     auto cvt_scales = [&](f16x2 (*ea)[2], f16x2 (*eb)[2]) {
