@@ -98,7 +98,9 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // the blocks under its 64 k of a chunk: 4, 2 or 1 bytes, fetched as the aligned dword holding them
 // and shifted into place when read.
 template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_tiled(
+// 128 x 128 tiles need few registers (64 accumulators per wave): two workgroups per CU, so a grid
+// a little larger than the CU count runs in one round; larger tiles one wave per SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <= 128 * 128) ? 2 : 1, (BM * BN <= 128 * 128) ? 2 : 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
     void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int m_off, int n_off, int splits,
