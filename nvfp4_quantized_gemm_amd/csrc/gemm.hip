@@ -765,14 +765,26 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
     }
     return pl;
   }
-  // fewer tiles than CUs: split K over idle CUs when every split keeps >= 8 chunks
+  // Fewer big tiles than CUs.  128x128 tiles run two workgroups per CU: when their grid fits one
+  // round (<= one per CU, or close to two per CU everywhere, or K short enough that the uneven
+  // share costs little) they beat splitting K over 256x256 tiles, whose partials cost HBM traffic
+  // and a reduction; a small grid with long K splits K two ways too (each split >= 16 chunks).
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t128 <= cus) {
+    pl.variant = GemmVariant::W4A4_128x128;
+    pl.splits = (2 * t128 <= cus && Kc >= 32 && N % 4 == 0) ? 2 : 1;
+    return pl;
+  }
+  if (t128 <= 2 * cus && (t128 % cus == 0 || t128 % cus >= (3 * cus) / 4 || Kc <= 12)) {
+    pl.variant = GemmVariant::W4A4_128x128;
+    return pl;
+  }
+  // otherwise 256x256 tiles, splitting K over idle CUs when every split keeps >= 8 chunks
   int best = 1;
   for (int sp = 2; sp <= 4; ++sp)
-    if (tb * sp <= cus && Kc / sp >= 8 && N % 4 == 0) best = sp;  // long K only: partials cost HBM traffic
+    if (tb * sp <= cus && Kc / sp >= 8 && N % 4 == 0) best = sp;
   if (tb * 2 > cus) best = 1;  // already more than half the chip: a reduction costs more than it saves
   pl.splits = best;
-  if (best == 1 && tb * 2 <= cus && (M + 127) / 128 * ((N + 127) / 128) <= 2 * cus)
-    pl.variant = GemmVariant::W4A4_128x128;  // small problem with short K: more, smaller tiles
   return pl;
 }
 
@@ -807,8 +819,15 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
       }
       return launch_tiled<0, 256, 256, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
     }
-    case GemmVariant::W4A4_128x128:
+    case GemmVariant::W4A4_128x128: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<0, 128, 128, 2, 2, OUT, ABLK>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, g.qo, stream);
+      }
       return launch_tiled<0, 128, 128, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
     case GemmVariant::W4A16_128x256: {
       if (pl.splits > 1) {
         float *part = static_cast<float *>(g.workspace);

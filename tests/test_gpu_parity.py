@@ -296,6 +296,20 @@ def test_gemm_w4a4_ragged(M, N, K):
     run_w4a4(x, w, torch.float32)
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (512, 512, 4096),     # 16 tiles of 128 x 128, K split two ways
+    (4096, 1024, 4096),   # 256 tiles of 128 x 128, one per CU
+    (2048, 4096, 1024),   # 512 tiles of 128 x 128, two per CU
+    (3072, 1408, 2048),   # 264 small tiles, uneven: 256 x 256 tiles with K split two ways
+])
+def test_gemm_w4a4_planner_paths(M, N, K):
+    """One shape per plan of the W4A4 planner below one round of 256 x 256 tiles (sampled outputs)."""
+    g = torch.Generator().manual_seed(M + N + K)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    run_w4a4(x, w, torch.bfloat16, sample=(64, 64))
+
+
 def test_gemm_w4a4_pixart_full_size_sampled():
     for name, x, w in workloads.pixart():
         run_w4a4(x, w, torch.bfloat16, sample=(96, 96))
