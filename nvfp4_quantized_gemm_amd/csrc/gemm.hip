@@ -29,7 +29,7 @@
 namespace nvfp4 {
 
 constexpr int kChunk = 128;  // k per LDS stage
-constexpr int64_t kW4A16TallM = 512;  // W4A16 rows from which 256-row tiles are used
+constexpr int64_t kW4A16TallM = 256;  // W4A16 rows from which 256-row tiles are considered
 constexpr bool kOutputNT = true;    // streaming stores for the bf16 / fp32 output
 constexpr bool kPartialNT = false;  // split-K partials (read back at once by the reduction)
 constexpr bool kReduceNT = false;   // the reduction reads the partials while they are still cached
@@ -743,15 +743,28 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
       pl.waves = per >= 48 ? 16 : (per >= 16 ? 8 : 4);
       return pl;
     }
-    // 256-row tiles reuse each dequantized B fragment for 8 MFMAs instead of 4 (B dequantization
-    // is the loop's VALU work); 128-row tiles keep small M from padding a 256-row tile
-    const bool tall = M >= kW4A16TallM;
-    pl.variant = tall ? GemmVariant::W4A16_256x256 : GemmVariant::W4A16_128x256;
-    const int64_t tb = ((M + (tall ? 255 : 127)) / (tall ? 256 : 128)) * ((N + 255) / 256);
-    int best = 1;
-    for (int sp = 2; sp <= 16; ++sp)
-      if (tb * sp <= cus && Kc / sp >= 6 && N % 4 == 0) best = sp;
-    pl.splits = best;
+    // 128 x 256 or 256 x 256 tiles (the latter reuse each dequantized B fragment for 8 MFMAs instead
+    // of 4) and a K split, by a cost model fit to measurements (M 64..4096, N and K 1024..12288):
+    // rounds of workgroups x chunks per split x a chunk's time for the tile, plus the fp32 partials'
+    // traffic (written, read back, output written) of a split.  Splits keep >= 6 chunks each.
+    double best_t = 1e300;
+    for (int cfg = 0; cfg < 2; ++cfg) {
+      if (cfg == 1 && M < kW4A16TallM) continue;
+      const int64_t bm = cfg ? 256 : 128;
+      const double chunk_us = cfg ? 3.71 : 1.99;
+      const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
+      for (int sp = 1; sp <= 16; ++sp) {
+        if (sp > 1 && (Kc / sp < 6 || N % 4 != 0)) continue;
+        const double rounds = (double)((tiles * sp + cus - 1) / cus);
+        double t = rounds * (double)((Kc + sp - 1) / sp) * chunk_us;
+        if (sp > 1) t += (8.0 * sp + 2.0) * (double)M * (double)N / 5.19e6;
+        if (t < best_t) {
+          best_t = t;
+          pl.variant = cfg ? GemmVariant::W4A16_256x256 : GemmVariant::W4A16_128x256;
+          pl.splits = sp;
+        }
+      }
+    }
     return pl;
   }
   const int64_t tmb = (M + 255) / 256, tnb = (N + 255) / 256, tb = tmb * tnb;
