@@ -5,26 +5,28 @@
 //
 // Lane-contiguous: a lane owns one 16-byte segment of the output (8 bf16 or 4 fp32 values), reads
 // its 4 or 2 code bytes and its block's scale byte, so every wave-wide store is one contiguous 1-KB
-// span and the code loads are contiguous too.  Each lane keeps four segments' loads in flight.
+// span and the code loads are contiguous too.  Each lane keeps four or eight segments' loads in
+// flight.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
 
 namespace {
-constexpr int kSegsPerLane = 4;
+// segments per lane: eight keep more bytes in flight on large tensors; small ones keep four, so
+// that the grid still has enough waves
+constexpr int kSegsSmall = 4, kSegsLarge = 8;
 constexpr bool kCodesNT = true;  // code bytes are read once: streaming loads
 constexpr bool kOutNT = true;    // the output is written once: streaming stores
 }
 
-template <int OUT, bool DENSE, int BLK>
+template <int OUT, bool DENSE, int BLK, int U>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ packed,
                                                     const uint8_t *__restrict__ scales,
                                                     const float *__restrict__ tensor_scale, uint64_t nseg,
                                                     FastDiv bpr, void *__restrict__ y, int64_t ld_y) {
   constexpr int E = (OUT == 1) ? 8 : 4;  // values per lane segment
   using Map = Segments<E, BLK>;  // a segment's block scale is byte g / Map::kLanesPerBlock
-  constexpr int U = kSegsPerLane;
   const float S = *tensor_scale;
   const int lane = threadIdx.x & 63;
   const uint64_t ntiles = (nseg + 64 * U - 1) / (64 * U);
@@ -85,30 +87,46 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
   }
 }
 
-template <int BLK>
+// one workgroup (four waves) per four tiles of U segments per lane, up to the cap
+template <int U>
+static unsigned dequantize_grid(uint64_t nseg) {
+  const uint64_t tiles = (nseg + 64 * U - 1) / (64 * U);
+  uint64_t g = (tiles + 3) / 4;
+  if (g < 1) g = 1;
+  return (unsigned)(g > (uint64_t)kDequantizeMaxGrid ? (uint64_t)kDequantizeMaxGrid : g);
+}
+
+template <int BLK, int U>
 static void run_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t K,
-                           uint64_t nseg, unsigned grid, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
+                           uint64_t nseg, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
   const FastDiv bpr = make_fastdiv((uint32_t)(K / BLK));
   const bool dense = (ld_y == K);
+  const unsigned grid = dequantize_grid<U>(nseg);
   if (out_dtype == 0) {
-    if (dense) k_dequantize<0, true, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-    else k_dequantize<0, false, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    if (dense) k_dequantize<0, true, BLK, U><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<0, false, BLK, U><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
   } else {
-    if (dense) k_dequantize<1, true, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
-    else k_dequantize<1, false, BLK><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    if (dense) k_dequantize<1, true, BLK, U><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
+    else k_dequantize<1, false, BLK, U><<<grid, 256, 0, stream>>>(packed, scales, tensor_scale, nseg, bpr, y, ld_y);
   }
+}
+
+template <int BLK>
+static void run_dequantize_u(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t K,
+                             uint64_t nseg, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
+  // eight segments per lane once that still gives >= 4 workgroups per CU
+  if (dequantize_grid<kSegsLarge>(nseg) >= 1024)
+    run_dequantize<BLK, kSegsLarge>(packed, scales, tensor_scale, K, nseg, y, out_dtype, ld_y, stream);
+  else
+    run_dequantize<BLK, kSegsSmall>(packed, scales, tensor_scale, K, nseg, y, out_dtype, ld_y, stream);
 }
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t M,
                              int64_t K, int blk, void *y, int out_dtype, int64_t ld_y, hipStream_t stream) {
   const uint64_t nseg = (uint64_t)M * (uint64_t)K / (out_dtype == 0 ? 4u : 8u);
-  const uint64_t tiles = (nseg + 64 * kSegsPerLane - 1) / (64 * kSegsPerLane);
-  uint64_t g = (tiles + 3) / 4;
-  if (g < 1) g = 1;
-  if (g > (uint64_t)kDequantizeMaxGrid) g = kDequantizeMaxGrid;
-  if (blk == 32) run_dequantize<32>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
-  else if (blk == 64) run_dequantize<64>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
-  else run_dequantize<16>(packed, scales, tensor_scale, K, nseg, (unsigned)g, y, out_dtype, ld_y, stream);
+  if (blk == 32) run_dequantize_u<32>(packed, scales, tensor_scale, K, nseg, y, out_dtype, ld_y, stream);
+  else if (blk == 64) run_dequantize_u<64>(packed, scales, tensor_scale, K, nseg, y, out_dtype, ld_y, stream);
+  else run_dequantize_u<16>(packed, scales, tensor_scale, K, nseg, y, out_dtype, ld_y, stream);
   return hipGetLastError();
 }
 

@@ -6,8 +6,13 @@
 namespace nvfp4 {
 
 constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pass (= partials)
-constexpr int kQuantizeMaxGrid = 2048;  // grid cap of the quantize kernel (grid-stride beyond)
-constexpr int kDequantizeMaxGrid = 4096;
+// Grid caps (grid-stride beyond).  The quantize kernel runs 2048 workgroups, all resident (8 per
+// CU), each prefetching its next tile; passes that write more than they read (static
+// quantization and fake quantization of large tensors) measured faster with 16384.  The
+// dequantize kernel, write-dominated too, runs one workgroup per four tiles up to a large cap.
+constexpr int kQuantizeMaxGrid = 2048;
+constexpr int kQuantizeWideGrid = 16384;
+constexpr int kDequantizeMaxGrid = 1 << 20;
 
 // blk: values per E4M3 scale byte along K (16, 32 or 64)
 hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, uint8_t *packed,

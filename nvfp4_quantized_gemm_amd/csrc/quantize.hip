@@ -243,7 +243,10 @@ template <int DT, bool DENSE, int YT, int BLK>
 static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr16, FastDiv bpr, uint8_t *packed,
                          uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, void *y, int64_t ld_y,
                          hipStream_t stream) {
-  const int gq = grid_for(nseg, kQuantizeMaxGrid);
+  // the dynamic NVFP4 pass keeps the resident grid (every workgroup also reduces the amax
+  // partials); the others widen it on large tensors
+  const bool wide = (!dynamic || YT >= 0) && grid_for(nseg, 1 << 30) > 4 * kQuantizeMaxGrid;
+  const int gq = grid_for(nseg, wide ? kQuantizeWideGrid : kQuantizeMaxGrid);
   if (dynamic) {
     const int ga = grid_for(nseg, kAmaxPartials);
     k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr16, partial);

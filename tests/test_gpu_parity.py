@@ -153,9 +153,31 @@ def test_quantize_near_tie_scales(S, dt):
 
 
 def test_quantize_sweep_full_size_largest():
-    """Largest sweep tensor (32768 x 12288 bf16, 403M values), dynamic, full comparison."""
+    """Largest sweep tensor (32768 x 12288 bf16, 403M values), dynamic, full comparison.  Then, at
+    the same size (the launch shapes the benchmark times: grid-stride over a capped grid, eight
+    segments per dequantize lane): static quantization with the dynamic S gives the same bytes,
+    dequantization to bf16 equals the oracle's bit for bit, and fake quantization (static and
+    dynamic) equals that dequantization."""
     x = workloads.sweep(32768, 12288)
-    assert_quantize_exact(x, label="sweep 32768x12288")
+    (p, s, S), (op, os_, oS) = assert_quantize_exact(x, label="sweep 32768x12288")
+    xd = x.to(DEV)
+    say("[static quantize, dequantize, fake quantize] 32768x12288")
+    p2, s2, _ = nv.nvfp4_quantize(xd, S.clone())
+    assert torch.equal(p2, p) and torch.equal(s2, s)
+    del p2, s2
+    y = nv.nvfp4_dequantize(p, s, S, torch.bfloat16)
+    _, y16_o = oracle.dequantize(op, os_, oS)
+    torch.cuda.synchronize()
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.nonzero(yb != y16_o)
+    assert bad[0].size == 0, f"{bad[0].size} dequantized values differ, first at {bad[0][0], bad[1][0]}"
+    del yb, y16_o
+    fs, _ = nv.nvfp4_fake_quantize(xd, S.clone())
+    assert torch.equal(fs.view(torch.int16), y.view(torch.int16))
+    del fs
+    fd, Sd = nv.nvfp4_fake_quantize(xd)
+    assert torch.equal(Sd, S)
+    assert torch.equal(fd.view(torch.int16), y.view(torch.int16))
 
 
 def test_quantize_deterministic():
@@ -167,9 +189,10 @@ def test_quantize_deterministic():
 
 # ---- dequantize -------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(4096, 1152), (17, 48)])
+# (8191, 3072): eight segments per lane, with a ragged last tile
+@pytest.mark.parametrize("M,K", [(4096, 1152), (17, 48), (8191, 3072)])
 def test_dequantize_exact_bits(M, K):
-    x = workloads.sweep(M, K) if M >= 4096 else torch.randn(M, K, generator=torch.Generator().manual_seed(3)).to(
+    x = workloads.sweep(M, K) if M == 4096 else torch.randn(M, K, generator=torch.Generator().manual_seed(3)).to(
         torch.bfloat16)
     say(f"[dequantize] {M}x{K}")
     (p, s, S), (op, os_, oS) = assert_quantize_exact(x, label="for dequant")
