@@ -732,7 +732,7 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   const int64_t Kc = K / kChunk;
   if (mode == 1) {
     const int64_t Nu = (N + 31) / 32;
-    if (M <= kSkinnyMaxM) {
+    if (M <= kSkinnyMaxM && 32 * lda < (int64_t(1) << 31)) {
       // streaming: >= ~1.5 workgroups per CU; narrow N splits K across workgroups (each split
       // keeps >= 16 chunks); waves per workgroup grow with the chunks per split
       pl.variant = GemmVariant::W4A16_Skinny;

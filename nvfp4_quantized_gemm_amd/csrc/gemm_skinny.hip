@@ -5,15 +5,24 @@
 //
 // Work split: workgroup (unit u, split s) owns the 32 output columns of prepacked unit u and the
 // 128-k chunks [s Kc / S, (s + 1) Kc / S); its NW waves (4, 8 or 16) take every NW-th chunk of
-// that range.  Per chunk a lane loads its two 16-byte code parts and
-// 4 scale bytes of the unit (the prepacked order is the MFMA operand order) plus its A row segment
-// and runs 8 bf16 MFMA steps with the weight fragment as the row operand: lane l = r + 32 h then
-// ends with output row m = r and, per group g, columns 8 g + 4 h + 0..3.  Rows r >= M load nothing
-// and contribute zeros.  Weight loads run three chunks ahead; each activation step slot is
-// reloaded for the next chunk as soon as its MFMA has consumed it.
+// that range.  Per chunk a lane loads its two 16-byte code parts and 4 scale bytes of the unit (the
+// prepacked order is the MFMA operand order) and runs 8 bf16 MFMA steps with the weight fragment
+// as the row operand and activation row r in lane l = r + 32 h: the lane ends with output row
+// m = r and, per group g, columns 8 g + 4 h + 0..3.  Rows r >= M are computed from duplicate rows
+// and never stored.  Weight loads run three chunks ahead in registers.
+//
+// Activations: in the MFMA operand order every lane holds a different row, so loading them in that
+// order touches 64 cache lines per instruction.  Instead each wave copies its chunk of the first
+// MR rows (MR = M rounded up to 4, 8, 16 or 32; 256 bytes per row) straight into a wave-private
+// LDS ring with row-contiguous 16-byte DMAs (16 lanes per row), L chunks ahead (L = 3, 3, 2, 1 by
+// MR, which keeps two workgroups of 8 waves per CU), and reads the operand order back from there.
+// The 16-byte pieces of row r are stored XOR-swizzled by r % 16, so that the 16 lanes of each read
+// pass hit 16 different bank groups.
 // The waves' accumulators are added in LDS in wave order (deterministic).  With S = 1 (wide N)
 // one kernel produces the output; narrow N splits K over S workgroups per unit so that enough
 // workgroups stream, and the split-K reduction kernel adds the S fp32 partials in order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,25 +45,63 @@ __device__ __forceinline__ bf16x8 dequant_b(uint32_t codes, float e) {
   return r;
 }
 
+// Activation ring of one wave: L slots of one chunk of MR rows each; MR / 4 DMAs fill a slot.
+template <int MR>
+struct SkinnyA {
+  static_assert(MR == 4 || MR == 8 || MR == 16 || MR == 32, "row classes");
+  static constexpr int kL = (MR <= 8) ? 3 : (MR == 16 ? 2 : 1);
+  static constexpr int kSlot = MR * 256;
+  static constexpr int kDma = MR / 4;
+};
+
+template <int NW, int MR>
+constexpr int skinny_lds_bytes() {
+  constexpr int ring = NW * SkinnyA<MR>::kL * SkinnyA<MR>::kSlot, red = NW * 16 * 64 * 4;
+  return ring > red ? ring : red;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// keeps the vector-memory issue order as written (the waits above count operations in that order)
+__device__ __forceinline__ void issue_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace
 
-template <int OUT, int NW>
+template <int OUT, int NW, int MR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_skinny(const uint16_t *__restrict__ a, int64_t lda,
                                                          const uint8_t *__restrict__ bp,
                                                          const float *__restrict__ b_ts, int M, int N, int K,
                                                          void *__restrict__ c, int64_t ldc, int splits,
                                                          float *__restrict__ partial) {
-  __shared__ float red[NW][16][64];
+  using SA = SkinnyA<MR>;
+  constexpr int L = SA::kL;
+  constexpr int NB = 3;            // vector-memory operations of one chunk's weight loads
+  constexpr int NA = SA::kDma;     // ... and of one chunk's activation DMAs
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int Kc = K / 128, Nu = (N + 31) / 32;
   const int u = blockIdx.x % Nu, split = blockIdx.x / Nu;
   const int kb = (int)((int64_t)split * Kc / splits), ke = (int)((int64_t)(split + 1) * Kc / splits);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
   const uint64_t scale_region = (uint64_t)Nu * (uint64_t)Kc * 2048ull;
-  const uint8_t *bcode = bp + (uint64_t)u * (uint64_t)Kc * 2048ull + lane * 16;
-  const uint8_t *bscale = bp + scale_region + (uint64_t)u * (uint64_t)Kc * 256ull + lane * 4;
+  // wave-uniform bases + 32-bit lane offsets (the loads take the scalar-base form)
+  const uint8_t *bcode = bp + (uint64_t)u * (uint64_t)Kc * 2048ull;
+  const uint8_t *bscale = bp + scale_region + (uint64_t)u * (uint64_t)Kc * 256ull;
+  const uint32_t lcode = (uint32_t)lane * 16u, lscale = (uint32_t)lane * 4u;
   const bool has_row = r < M;
-  const uint16_t *arow = a + (int64_t)(has_row ? r : 0) * lda + 64 * h;
+
+  // DMA q of a chunk: lane l takes row 4 q + l / 16 (rows past M re-read row M - 1) and lands at
+  // LDS unit 64 q + l of the slot, i.e. row-major 256-byte rows holding piece (l % 16) ^ (row % 16).
+  // Lane-dependent offsets are recomputed per chunk from an opaque copy of the lane index (a few
+  // VALU operations) rather than kept live across the loop.
+  // (byte offsets within a chunk column: 32 lda < 2^31 is a condition of this kernel's plan)
+  uint8_t *aring = smem + wave * (L * SA::kSlot);
 
   struct BRegs {
     u32x4 code[2];  // parts 0 and 1: dword s & 3 of part s >> 2 holds MFMA step s
@@ -62,18 +109,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   };
   auto load_b = [&](int kc, BRegs &x) {
     const uint8_t *pc = bcode + (uint64_t)kc * 2048ull;
-    x.code[0] = load16<true>(pc);  // streaming: each weight byte is read once per call
-    x.code[1] = load16<true>(pc + 1024);
-    x.sc = *reinterpret_cast<const uint32_t *>(bscale + (uint64_t)kc * 256ull);
+    x.code[0] = load16<true>(pc + lcode);  // streaming: each weight byte is read once per call
+    x.code[1] = load16<true>(pc + (lcode + 1024u));
+    x.sc = *reinterpret_cast<const uint32_t *>(bscale + (uint64_t)kc * 256ull + lscale);
   };
-  auto load_a = [&](int kc, u32x4 *x) {
-    const uint16_t *pa = arow + (int64_t)kc * 128;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      x[s] = has_row ? *reinterpret_cast<const u32x4 *>(pa + 8 * s) : z;
-    }
-  };
+  // wave w takes chunks kb + w + i NW, i = 0 .. nw - 1
+  const int nw = (kb + wave < ke) ? (ke - kb - wave + NW - 1) / NW : 0;
+  auto chunk_of = [&](int i) { return kb + wave + i * NW; };
 
   f32x16 acc0, acc1;
 #pragma unroll
@@ -81,42 +123,87 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     acc0[v] = 0.0f;
     acc1[v] = 0.0f;
   }
-  // wave w takes chunks w, w + NW, ...; weight loads run two chunks ahead, activation loads one
-  // wave w takes chunks w, w + NW, ...  Weight loads go into a 3-slot ring (slot j holds chunks
-  // i = j mod 3 of the wave's sequence; a slot is refilled three chunks ahead right after use; the
-  // loop is unrolled by 3 so slots never move between registers, which would wait on the loads).
-  if (kb + wave < ke) {
+  // Issue order, chunk i: activation DMAs of chunk i + L into the slot chunk i has just read, then
+  // weight loads of chunk i + 3 into register slot i % 3 (the loop is unrolled by 3 so slots never
+  // move between registers); the prologue issues the same pattern for the virtual chunks -3 .. -1,
+  // and nothing past the wave's last chunk is issued.  So when chunk i starts, the operations
+  // issued after its activation DMAs are the weight loads of the chunks i - L + 3 .. i + 2 and the
+  // DMAs of the chunks i + 1 .. i + L - 1 that exist: with t = nw - i chunks left, L weight groups
+  // and L - 1 DMA groups for t >= 3, L - 1 and min(1, L - 1) for t = 2, max(L - 2, 0) and none
+  // for t = 1.
+  if (nw > 0) {
     BRegs b[3];
-    u32x4 av[8];
+    auto issue_a = [&](int i, int slot) {  // the wave's chunk i into ring slot `slot`
+      const uint8_t *src = reinterpret_cast<const uint8_t *>(a) + (int64_t)chunk_of(i) * 256;
+      uint8_t *dst = aring + slot * SA::kSlot;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (kb + wave + j * NW < ke) load_b(kb + wave + j * NW, b[j]);
-    load_a(kb + wave, av);
-#pragma unroll 1
-    for (int i0 = 0; kb + wave + i0 * NW < ke; i0 += 3) {
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int kc = kb + wave + (i0 + j) * NW;
-        if (kc < ke) {
-          const bool more = kc + NW < ke;
-          float e[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) e[t] = e4m3_to_f32((b[j].sc >> (8 * t)) & 0xffu);
-          const uint16_t *pa_next = arow + (int64_t)(kc + NW) * 128;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const bf16x8 bf = dequant_b(b[j].code[s >> 2][s & 3], e[s >> 1]);
-            const bf16x8 af = __builtin_bit_cast(bf16x8, av[s]);
-            if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc1, 0, 0, 0);
-            else acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc0, 0, 0, 0);
-            // rolling activation prefetch: this step's slot now loads the next chunk's step
-            if (more && has_row) av[s] = *reinterpret_cast<const u32x4 *>(pa_next + 8 * s);
-          }
-          if (kc + 3 * NW < ke) load_b(kc + 3 * NW, b[j]);
-        }
+      for (int q = 0; q < SA::kDma; ++q) {
+        const int row = 4 * q + (ln >> 4);
+        const uint32_t off = 2u * ((uint32_t)min(row, M - 1) * (uint32_t)lda) + 16u * (uint32_t)((ln & 15) ^ (row & 15));
+        g2l16(src + off, dst + q * 1024);
       }
+    };
+#pragma unroll
+    for (int v = -3; v < 0; ++v) {
+      if (v + L >= 0 && v + L < nw) issue_a(v + L, v + L);
+      issue_order();
+      if (v + 3 < nw) load_b(chunk_of(v + 3), b[v + 3]);
+      issue_order();
     }
+    // chunk i with its weights in register slot J
+    auto body = [&](int i, auto slot_tag) {
+      constexpr int J = decltype(slot_tag)::value;
+      {
+        const int t = nw - i;
+        constexpr int L2 = (L >= 2) ? L - 2 : 0, NA2 = (L >= 2) ? NA : 0;
+        if (t >= 3) wait_vmcnt<L * NB + (L - 1) * NA>();
+        else if (t == 2) wait_vmcnt<(L - 1) * NB + NA2>();
+        else wait_vmcnt<L2 * NB>();
+      }
+      const int sl = i % L;
+      // operand read of step s: row r % MR, piece 8 h + s, i.e. 16-byte unit (8 h + s) ^ (r % 16)
+      // of the row = ((8 h) ^ (r % 16)) ^ s
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int rrow = ln & 31 & (MR - 1), y = (8 * (ln >> 5)) ^ (rrow & 15);
+      const uint8_t *rd = aring + sl * SA::kSlot + rrow * 256;
+      u32x4 av[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const u32x4 *>(rd + ((y ^ s) << 4));
+      // the slot is refilled next: its reads must have completed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (i + L < nw) issue_a(i + L, sl);
+      issue_order();
+      float e[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) e[t] = e4m3_to_f32((b[J].sc >> (8 * t)) & 0xffu);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 bf = dequant_b(b[J].code[s >> 2][s & 3], e[s >> 1]);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, av[s]);
+        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc0, 0, 0, 0);
+      }
+      issue_order();
+      if (i + 3 < nw) load_b(chunk_of(i + 3), b[J]);
+      issue_order();
+    };
+    int i0 = 0;
+#pragma unroll 1
+    for (; i0 + 3 <= nw; i0 += 3) {
+      body(i0, std::integral_constant<int, 0>{});
+      body(i0 + 1, std::integral_constant<int, 1>{});
+      body(i0 + 2, std::integral_constant<int, 2>{});
+    }
+    if (i0 < nw) body(i0, std::integral_constant<int, 0>{});
+    if (i0 + 1 < nw) body(i0 + 1, std::integral_constant<int, 1>{});
+    wait_vmcnt<0>();  // every DMA has landed before the LDS is reused
   }
+  // the reduction below reuses the LDS of the activation rings
+  __syncthreads();
+  float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(smem);
 #pragma unroll
   for (int v = 0; v < 16; ++v) red[wave][v][lane] = acc0[v] + acc1[v];
   __syncthreads();
@@ -175,20 +262,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+template <int OUT, int NW, int MR>
+static hipError_t launch_skinny_cfg(const GemmArgs &g, int splits, float *partial, hipStream_t stream) {
+  constexpr int smem = skinny_lds_bytes<NW, MR>();
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_skinny<OUT, NW, MR>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int Nu = (int)((g.N + 31) / 32);
+  k_gemm_skinny<OUT, NW, MR><<<(unsigned)(Nu * splits), NW * 64, smem, stream>>>(
+      static_cast<const uint16_t *>(g.a), g.lda, static_cast<const uint8_t *>(g.b), g.b_ts, (int)g.M, (int)g.N,
+      (int)g.K, g.c, g.ldc, splits, partial);
+  return hipGetLastError();
+}
+
+template <int OUT, int NW>
+static hipError_t launch_skinny_rows(const GemmArgs &g, int splits, float *partial, hipStream_t stream) {
+  if (g.M <= 4) return launch_skinny_cfg<OUT, NW, 4>(g, splits, partial, stream);
+  if (g.M <= 8) return launch_skinny_cfg<OUT, NW, 8>(g, splits, partial, stream);
+  if (g.M <= 16) return launch_skinny_cfg<OUT, NW, 16>(g, splits, partial, stream);
+  return launch_skinny_cfg<OUT, NW, 32>(g, splits, partial, stream);
+}
+
 template <int OUT>
 static hipError_t launch_skinny_out(const GemmArgs &g, int nw, int splits, float *partial, hipStream_t stream) {
-  const int Nu = (int)((g.N + 31) / 32);
-  const unsigned grid = (unsigned)(Nu * splits);
-  const uint16_t *a = static_cast<const uint16_t *>(g.a);
-  const uint8_t *b = static_cast<const uint8_t *>(g.b);
-  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-  if (nw >= 16)
-    k_gemm_skinny<OUT, 16><<<grid, 1024, 0, stream>>>(a, g.lda, b, g.b_ts, M, N, K, g.c, g.ldc, splits, partial);
-  else if (nw >= 8)
-    k_gemm_skinny<OUT, 8><<<grid, 512, 0, stream>>>(a, g.lda, b, g.b_ts, M, N, K, g.c, g.ldc, splits, partial);
-  else
-    k_gemm_skinny<OUT, 4><<<grid, 256, 0, stream>>>(a, g.lda, b, g.b_ts, M, N, K, g.c, g.ldc, splits, partial);
-  return hipGetLastError();
+  if (nw >= 16) return launch_skinny_rows<OUT, 16>(g, splits, partial, stream);
+  if (nw >= 8) return launch_skinny_rows<OUT, 8>(g, splits, partial, stream);
+  return launch_skinny_rows<OUT, 4>(g, splits, partial, stream);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *partial, hipStream_t stream) {

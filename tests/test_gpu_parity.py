@@ -379,6 +379,9 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 96, 256), (37, 200, 1152), (300, 130, 384), (5, 48, 80),
                                    # streaming kernel (M <= 32): K split over workgroups, ragged last unit
                                    (1, 1000, 2048), (31, 1000, 2048), (7, 98, 1536), (16, 4096, 3072), (3, 200, 4096),
+                                   # each activation row class of the streaming kernel (4, 8, 16, 32 rows),
+                                   # full and partly filled
+                                   (4, 520, 1152), (9, 300, 1152), (17, 1000, 2048), (32, 4096, 3072),
                                    # tiled kernel with K split
                                    (200, 520, 2048),
                                    # 256-row tiles (half-chunk stages): ragged M and N, K split, 9 chunks
@@ -388,6 +391,29 @@ def test_gemm_w4a16_ragged(M, N, K):
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = workloads.laplace_tailed_weight(N, K, g)
     run_w4a16(a, w, torch.float32)
+
+
+@pytest.mark.parametrize("M", [1, 9, 17, 32, 300])
+def test_gemm_w4a16_strided_activation(M):
+    """A row-strided activation view (lda = K + 64, the padding holds 1e30 and must be ignored):
+    streaming kernel for each row class, tiled kernel for M = 300."""
+    N, K = 520, 1152
+    g = torch.Generator().manual_seed(900 + M)
+    a = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = workloads.laplace_tailed_weight(N, K, g)
+    say(f"[gemm W4A16 strided] M={M} N={N} K={K} lda={K + 64}")
+    bp, Sb, _ = prepare_weight(w)
+    big = torch.full((M, K + 64), 1e30, dtype=torch.bfloat16)
+    big[:, :K] = a
+    ad = big.to(DEV)[:, :K]
+    out = nv.nvfp4_gemm(nv.W4A16, ad, None, None, bp, Sb, N, K, torch.float32)
+    torch.cuda.synchronize()
+    wo = np_x(w)
+    SB = oracle.tensor_scale(wo)
+    bo_p, bo_s, _ = oracle.quantize(wo, S=SB)
+    B, _ = oracle.dequantize(bo_p, bo_s, SB)
+    Y, R = oracle.gemm(oracle.bf16_to_f32(np_bf16(a)), B)
+    check_gemm(out.cpu().numpy(), Y, R, False, f"W4A16 strided {M}x{N}x{K}")
 
 
 def test_gemm_w4a16_full_size():
