@@ -199,7 +199,6 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 #endif
 
 namespace {
-constexpr int kMxTileM = 256;
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v8i as_v8(const u32x4 &v) {
@@ -223,33 +222,42 @@ __device__ __forceinline__ int frag_off(int grp, int t, int lane) {
   return (2 * grp + (r >> 4)) * 1024 + (16 * (2 * t + h) + (r & 15)) * 16;
 }
 
-template <int WM, int WN, int SX>
+// T x T tile (T = 256 or 128) of WM x WN waves
+template <int T, int WM, int WN, int SX>
 struct MxCfg {
   static constexpr int kWaves = WM * WN;
-  static constexpr int kTM = 8 / WM, kTN = 8 / WN;  // 32 x 32 tiles per wave
-  static constexpr int kCodes = 8 * 2 * 1024;       // one operand's codes of a chunk
+  static constexpr int kTM = T / 32 / WM, kTN = T / 32 / WN;  // 32 x 32 tiles per wave
+  static constexpr int kBlocks = T / 16;                      // 16-row blocks per operand
+  static constexpr int kCodes = kBlocks * 1024;               // one operand's codes of a chunk
   static constexpr int kStage = 2 * kCodes;
   static constexpr int kStages = 4;
-  static constexpr int kScaleBlk = 16 * 256;                    // one operand's scale words of 4 chunks
-  static constexpr int kScaleBase = kStages * kStage;           // [2 slots][A, B][kScaleBlk]
+  static constexpr int kScaleBlk = 16 * T;                    // one operand's scale words of 4 chunks
+  static constexpr int kScaleBase = kStages * kStage;         // [2 slots][A, B][kScaleBlk]
   static constexpr int kLds = kScaleBase + 2 * 2 * kScaleBlk;
-  // DMA loads per wave: codes 16 per operand per chunk; scales per 4 chunks 16 per operand with one
-  // word per lane (SX = 1), or 4 per operand with a row's 4 words per lane (SX = 4)
-  static constexpr int kNC = 16 / kWaves, kNS = 16 / kWaves, kNS4 = 8 / kWaves;
+  // DMA loads per wave: codes T / 16 per operand per chunk; scales per 4 chunks T / 16 per operand
+  // with one word per lane (SX = 1), or T / 64 per operand with a row's 4 words per lane (SX = 4)
+  static constexpr int kQ4 = T / 64;
+  static constexpr int kNC = kBlocks / kWaves, kNS = kBlocks / kWaves, kNS4 = 2 * kQ4 / kWaves;
   static constexpr int kSlots = 2 * kNC;                       // per chunk
   static constexpr int kSSlots = (SX == 1) ? 2 * kNS : kNS4;   // per scale block
-  static_assert(kNC * kWaves == 16 && kNS * kWaves == 16 && kNS4 * kWaves == 8, "even DMA split");
+  static_assert(kNC * kWaves == kBlocks && kNS4 * kWaves == 2 * kQ4, "even DMA split");
+  static_assert(kTM * WM * 32 == T && kTN * WN * 32 == T, "wave tiling");
   static_assert(SX == 1 || SX == 4, "scale words per DMA lane");
   static_assert(kLds <= 160 * 1024, "LDS fits");
 };
 }  // namespace
 
-template <int OUT, int WM, int WN, int SX>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void k_mx_gemm(
+// waves per SIMD: one 256-tile workgroup per CU (2 x 4 waves: two per SIMD), or two 128-tile
+// workgroups of 2 x 2 waves
+template <int T, int WM, int WN>
+constexpr int mx_waves_per_eu() { return T == 256 ? WM * WN / 4 : 2 * WM * WN / 4; }
+
+template <int OUT, int T, int WM, int WN, int SX>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(mx_waves_per_eu<T, WM, WN>(), mx_waves_per_eu<T, WM, WN>()))) void k_mx_gemm(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ as, const uint8_t *__restrict__ b,
     const uint8_t *__restrict__ bs, int M, int N, int K, void *__restrict__ c, int64_t ldc, int tiles_m,
     int tiles_n) {
-  using Cfg = MxCfg<WM, WN, SX>;
+  using Cfg = MxCfg<T, WM, WN, SX>;
   constexpr int TM = Cfg::kTM, TN = Cfg::kTN, S = Cfg::kStages, W = Cfg::kWaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -266,11 +274,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   }
   int tmi, tni;
   grouped_tile<4>(bid, tiles_m, tiles_n, tmi, tni);
-  const int m0 = tmi * kMxTileM, n0 = tni * kMxTileM;
+  const int m0 = tmi * T, n0 = tni * T;
   const int nk = K / 128;
   const uint32_t rowb = (uint32_t)(K / 2), srow = (uint32_t)(K / 32);  // bytes per codes / scales row
 
-  // DMA sources: wave-uniform tile bases + 32-bit lane offsets (host: 256 * rowb < 2^31)
+  // DMA sources: wave-uniform tile bases + 32-bit lane offsets (host: T * rowb < 2^31)
   const uint8_t *a_tile = a + (int64_t)m0 * rowb, *as_tile = as + (int64_t)m0 * srow;
   const uint8_t *b_tile = b + (int64_t)n0 * rowb, *bs_tile = bs + (int64_t)n0 * srow;
   uint32_t oa[Cfg::kNC], ob[Cfg::kNC];
@@ -294,10 +302,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   } else {
 #pragma unroll
     for (int i = 0; i < Cfg::kNS4; ++i) {
-      // scale DMA q (0..7) covers operand q / 4, rows 64 (q % 4) .. + 63, one row per lane
-      const int q = wave + W * i, row64 = 64 * (q & 3) + lane;
-      osx[i] = (q >> 2) ? (uint32_t)(min(n0 + row64, N - 1) - n0) * srow
-                        : (uint32_t)(min(m0 + row64, M - 1) - m0) * srow;
+      // scale DMA q (0 .. 2 T / 64 - 1) covers operand q / (T / 64), rows 64 (q % (T / 64)) .. + 63,
+      // one row per lane
+      const int q = wave + W * i, row64 = 64 * (q % Cfg::kQ4) + lane;
+      osx[i] = (q / Cfg::kQ4) ? (uint32_t)(min(n0 + row64, N - 1) - n0) * srow
+                              : (uint32_t)(min(m0 + row64, M - 1) - m0) * srow;
     }
   }
   auto issue = [&](int kc, int stage) {
@@ -323,8 +332,8 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
       const uint32_t kcw = (uint32_t)min(blk, nk / 4 - 1) * 16u;
 #pragma unroll
       for (int i = 0; i < Cfg::kNS4; ++i) {
-        const int q = wave + W * i;
-        g2l16(((q >> 2) ? bs_tile : as_tile) + (osx[i] + kcw), sl + (q >> 2) * Cfg::kScaleBlk + (q & 3) * 1024);
+        const int q = wave + W * i, op = q / Cfg::kQ4;
+        g2l16((op ? bs_tile : as_tile) + (osx[i] + kcw), sl + op * Cfg::kScaleBlk + (q % Cfg::kQ4) * 1024);
       }
     }
   };
@@ -413,10 +422,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM
   __syncthreads();
   typedef typename std::conditional<OUT == 0, float, __bf16>::type OutT;
   const bool vec = (ldc * (int64_t)sizeof(OutT)) % 16 == 0;
-  constexpr int CW = 256 / WN;  // columns per wave
+  constexpr int CW = T / WN;  // columns per wave
   static_assert(W * 32 * EpiPitch<CW, 4>::kPitch <= S * Cfg::kStage, "epilogue staging fits the LDS ring");
   uint8_t *lds_wave = smem + wave * (32 * EpiPitch<CW, 4>::kPitch);
-  store_tile<CW, TM, TN, OutT, true>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * (256 / WM), n0 + wn * CW,
+  store_tile<CW, TM, TN, OutT, true>(acc, 1.0f, static_cast<OutT *>(c), ldc, M, N, m0 + wm * (T / WM), n0 + wn * CW,
                                      vec, lds_wave, lane);
 }
 
@@ -475,22 +484,34 @@ hipError_t launch_mx_dequantize(const uint8_t *packed, const uint8_t *scales, in
   return hipGetLastError();
 }
 
-template <int OUT, int WM, int WN, int SX>
+template <int OUT, int T, int WM, int WN, int SX>
 static hipError_t launch_mx_tiled(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,
                                   int64_t N, int64_t K, void *c, int64_t ldc, hipStream_t stream) {
-  using Cfg = MxCfg<WM, WN, SX>;
-  const int tm = (int)((M + kMxTileM - 1) / kMxTileM), tn = (int)((N + kMxTileM - 1) / kMxTileM);
+  using Cfg = MxCfg<T, WM, WN, SX>;
+  const int tm = (int)((M + T - 1) / T), tn = (int)((N + T - 1) / T);
   constexpr int smem = Cfg::kLds;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, WM, WN, SX>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, T, WM, WN, SX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  k_mx_gemm<OUT, WM, WN, SX><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c,
-                                                                         ldc, tm, tn);
+  k_mx_gemm<OUT, T, WM, WN, SX><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c,
+                                                                            ldc, tm, tn);
   return hipGetLastError();
+}
+
+// Tile choice: 128 x 128 tiles (up to two workgroups per CU) when 256 x 256 tiles (one per CU)
+// would leave CUs idle and the small tiles still fit one round, i.e. at most two per CU of the
+// chip's 256.  A lone 128-tile workgroup runs a chunk in ~0.56x the time of a 256-tile one for a
+// quarter of the work, so the small tiles win only by occupying more CUs (4096 x 1152 x 1152:
+// 14.3 -> 11.0 us, 2048^3: 21.7 -> 12.1 us) and lose once they need more than one round (4096 x
+// 3456 x 1152, 864 tiles: 18.7 -> 21.7 us).
+static bool mx_use_small_tiles(int64_t M, int64_t N) {
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  return t256 < 256 && t128 <= 2 * 256;
 }
 
 template <int OUT>
@@ -505,8 +526,12 @@ static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const 
   // a row's 4 scale words of a 4-chunk block are one 16-byte DMA lane when rows (K / 32 bytes)
   // and both scale arrays are 16-byte aligned
   const bool sx4 = K % 512 == 0 && reinterpret_cast<uintptr_t>(as) % 16 == 0 && reinterpret_cast<uintptr_t>(bs) % 16 == 0;
-  if (sx4) return launch_mx_tiled<OUT, MX_WM, MX_WN, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
-  return launch_mx_tiled<OUT, MX_WM, MX_WN, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
+  if (mx_use_small_tiles(M, N)) {
+    if (sx4) return launch_mx_tiled<OUT, 128, 2, 2, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
+    return launch_mx_tiled<OUT, 128, 2, 2, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
+  }
+  if (sx4) return launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
+  return launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
 }
 
 hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,

@@ -150,6 +150,16 @@ def test_mx_gemm_ragged(M, N, K):
     run_mx_gemm(x, w, torch.float32)
 
 
+@pytest.mark.parametrize("K", [256, 512])
+def test_mx_gemm_256_tiles_ragged(K):
+    """Enough output for 256 x 256 tiles (17 x 17 of them, ragged on both sides), full comparison;
+    the smaller shapes above run 128 x 128 tiles."""
+    g = torch.Generator().manual_seed(K)
+    x = torch.randn(4100, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(4130, K, generator=g)).to(torch.bfloat16)
+    run_mx_gemm(x, w, torch.float32)
+
+
 def test_mx_gemm_scales_4_byte_aligned():
     """Scale arrays that are 4- but not 16-byte aligned with K % 512 == 0: the 4-byte scale loads."""
     g = torch.Generator().manual_seed(4)
