@@ -526,12 +526,31 @@ static hipError_t launch_mx_gemm_out(const uint8_t *a, const uint8_t *as, const 
   // a row's 4 scale words of a 4-chunk block are one 16-byte DMA lane when rows (K / 32 bytes)
   // and both scale arrays are 16-byte aligned
   const bool sx4 = K % 512 == 0 && reinterpret_cast<uintptr_t>(as) % 16 == 0 && reinterpret_cast<uintptr_t>(bs) % 16 == 0;
-  if (mx_use_small_tiles(M, N)) {
-    if (sx4) return launch_mx_tiled<OUT, 128, 2, 2, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
-    return launch_mx_tiled<OUT, 128, 2, 2, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
+  auto small = [&](const uint8_t *bb, const uint8_t *bbs, int64_t n, void *cc) {
+    return sx4 ? launch_mx_tiled<OUT, 128, 2, 2, 4>(a, as, bb, bbs, M, n, K, cc, ldc, stream)
+               : launch_mx_tiled<OUT, 128, 2, 2, 1>(a, as, bb, bbs, M, n, K, cc, ldc, stream);
+  };
+  auto big = [&](int64_t n) {
+    return sx4 ? launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 4>(a, as, b, bs, M, n, K, c, ldc, stream)
+               : launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 1>(a, as, b, bs, M, n, K, c, ldc, stream);
+  };
+  if (mx_use_small_tiles(M, N)) return small(b, bs, N, c);
+  // More than one round of 256 x 256 tiles: when the columns that make exactly one round leave a
+  // remainder of at most one 128 x 128 tile per CU, run that remainder as a second launch of
+  // small tiles instead of a second, mostly idle round of big ones.  B and C of the remainder are
+  // the same arrays from column n_big on (B rows and scale rows are whole rows).
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, cols = 256 / tm;
+  if (tm * tn > 256 && cols >= 1 && cols < tn) {
+    const int64_t n_big = cols * 256;
+    const int64_t rest = ((M + 127) / 128) * ((N - n_big + 127) / 128);
+    if (rest <= 256) {
+      hipError_t e = big(n_big);
+      if (e != hipSuccess) return e;
+      const size_t esz = OUT == 0 ? 4 : 2;
+      return small(b + n_big * (K / 2), bs + n_big * (K / 32), N - n_big, static_cast<uint8_t *>(c) + n_big * esz);
+    }
   }
-  if (sx4) return launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 4>(a, as, b, bs, M, N, K, c, ldc, stream);
-  return launch_mx_tiled<OUT, 256, MX_WM, MX_WN, 1>(a, as, b, bs, M, N, K, c, ldc, stream);
+  return big(N);
 }
 
 hipError_t launch_mx_gemm(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int64_t M,

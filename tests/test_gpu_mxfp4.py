@@ -160,6 +160,16 @@ def test_mx_gemm_256_tiles_ragged(K):
     run_mx_gemm(x, w, torch.float32)
 
 
+@pytest.mark.parametrize("K", [256, 512])
+def test_mx_gemm_mixed_tiles_ragged(K):
+    """17 columns of 256 x 256 tiles over 16 row tiles: one round of big tiles on the first 4096
+    columns, the ragged last 200 columns as a second launch of 128 x 128 tiles; full comparison."""
+    g = torch.Generator().manual_seed(3 * K)
+    x = torch.randn(4096, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(4296, K, generator=g)).to(torch.bfloat16)
+    run_mx_gemm(x, w, torch.bfloat16)
+
+
 def test_mx_gemm_scales_4_byte_aligned():
     """Scale arrays that are 4- but not 16-byte aligned with K % 512 == 0: the 4-byte scale loads."""
     g = torch.Generator().manual_seed(4)
