@@ -170,11 +170,11 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 
 // ---- GEMM: Y[M][N] = A[M][K] B[N][K]^T, both operands canonical MXFP4 ---------------------------------
 //
-// 256 x 256 tile per workgroup of WM x WN waves, each owning (256 / WM) x (256 / WN) = TM x TN
-// tiles of 32 x 32: 2 x 2 waves (one per SIMD, 128 x 128 each) or 2 x 4 waves (two per SIMD,
-// 128 x 64 each, so one wave's LDS and DMA waits overlap the other's MFMAs).  K in chunks of 128
-// (two 64-k MFMA steps).  LDS stage (32 KB):
-//   A codes  [16 blocks of 16 rows][4 pieces][16 rows][16 B]   B codes likewise (columns).
+// T x T tile per workgroup of WM x WN waves, each owning (T / WM) x (T / WN) = TM x TN tiles of
+// 32 x 32.  T = 256: 2 x 4 waves (two per SIMD, 128 x 64 each, so one wave's LDS and DMA waits
+// overlap the other's MFMAs), one workgroup per CU.  T = 128: 2 x 2 waves of 64 x 64, two
+// workgroups per CU.  K in chunks of 128 (two 64-k MFMA steps).  LDS stage (T / 8 KB):
+//   A codes  [T / 16 blocks of 16 rows][4 pieces][16 rows][16 B]   B codes likewise (columns).
 // A codes block holds 16 rows x the chunk's 64 bytes each, piece-major, so one DMA reads whole
 // 64-byte row segments and every 16-lane LDS read pass is contiguous; MFMA lane (r, h) of step s
 // reads piece 2 s + h of row r (k-half h of the step).  A 4-stage ring with the DMA three chunks
@@ -182,13 +182,13 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict
 // barrier per chunk.
 // Scales come in blocks of 4 chunks, double-buffered beside the ring: a row's scale word of a
 // chunk (its 4 bytes, 4-byte aligned in the canonical [rows][K/32] layout) is one 4-byte
-// DMA lane, and one DMA covers 16 rows x 4 chunks (lane = 16 * chunk + row), so an operand's 256
-// rows take 16 DMAs per 4 chunks:  scale block [16 row blocks][4 chunks][16 rows][4 B].  Block
+// DMA lane, and one DMA covers 16 rows x 4 chunks (lane = 16 * chunk + row), so an operand's T
+// rows take T / 16 DMAs per 4 chunks:  scale block [T / 16 row blocks][4 chunks][16 rows][4 B].  Block
 // j + 1 is issued in the first chunk of block j, after that chunk's codes, and is needed from the
 // look-ahead read of chunk 4 j + 4 on (three chunks later); the chunk waits account for it.  When
 // K % 512 == 0 and both scale arrays are 16-byte aligned, rows of scales are 16-byte aligned and a
-// row's 4 words of a block are one 16-byte DMA lane instead (SX = 4: 4 DMAs per operand per block,
-// block layout [256 rows][4 chunks][4 B]).  Of a
+// row's 4 words of a block are one 16-byte DMA lane instead (SX = 4: T / 64 DMAs per operand per
+// block, block layout [T rows][4 chunks][4 B]).  Of a
 // word, block 2 s + h feeds the MFMA: the lane shifts the word right by 8 h and op_sel picks byte
 // 2 s.  Rows past M / N are clamped to the last one (never stored), chunks past K to the last.
 #ifndef MX_WM
