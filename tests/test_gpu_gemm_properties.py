@@ -1,0 +1,97 @@
+"""GPU property tests of the GEMMs over shapes: Hypothesis draws M, N, K (whole 128-k chunks or
+not, ragged tile edges, one row to a few thousand), the mode (W4A4 at block sizes 16 / 32 / 64,
+W4A16, MXFP4) and the output type, so the planners' every plan is reached (256x256 and 128x128
+tiles, the mixed plan, K splits, the streaming kernel's row classes and splits, the generic kernel).
+Each case compares sampled output rows and columns with the oracle's dequantize-then-fp64-matmul
+of the oracle's own quantization: within 1e-5 sum|a b| per element (fp32 output), plus the bf16
+rounding for bf16 output [NVFP4-DiT page, Methodology section 3; vllm-omni NVFP4 RFC, Open
+Question 1].  Draws are derandomized, so every run sees the same cases."""
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, example, given, settings
+from hypothesis import strategies as st
+
+import nvfp4_quantized_gemm_amd as nv
+import oracle
+from test_gpu_parity import DEV, check_gemm, np_x, say
+
+pytestmark = pytest.mark.gpu
+
+SETTINGS = settings(max_examples=100, deadline=None, derandomize=True,
+                    suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+
+
+@st.composite
+def gemm_case(draw):
+    mode = draw(st.sampled_from(["w4a4", "w4a4_b32", "w4a4_b64", "w4a16", "mx"]))
+    M = draw(st.one_of(st.integers(1, 40), st.integers(41, 700), st.integers(701, 4200)))
+    N = draw(st.one_of(st.integers(1, 300), st.integers(301, 4700)))
+    if mode == "w4a16" and N % 4 and draw(st.booleans()):
+        N += 4 - N % 4  # narrow N with K splits needs N % 4 == 0; also draw the others
+    kb = 64 if mode == "w4a4_b64" else (32 if mode in ("w4a4_b32", "mx") else 16)
+    whole = draw(st.booleans())
+    if whole:
+        K = 128 * draw(st.integers(1, 40))
+    else:
+        K = kb * draw(st.integers(1, 80))
+    out = draw(st.sampled_from([torch.float32, torch.bfloat16]))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    return mode, M, N, K, out, seed
+
+
+@SETTINGS
+@given(gemm_case())
+# besides the draws, which lean to small shapes: one case per large plan
+@example(("w4a4", 4096, 1152, 4608, torch.bfloat16, 11))    # 256x256 tiles, three-way K split
+@example(("w4a4", 4096, 4608, 1152, torch.bfloat16, 12))    # one round of 256 tiles + 128 tiles
+@example(("w4a4_b32", 4100, 3000, 1024, torch.float32, 13))  # two rounds of 256 tiles
+@example(("w4a4", 512, 512, 4096, torch.float32, 14))       # 128x128 tiles, two-way K split
+@example(("w4a16", 1024, 3072, 3072, torch.bfloat16, 15))   # 256x256 W4A16 tiles
+@example(("w4a16", 300, 12288, 3072, torch.float32, 16))    # 128x256 W4A16 tiles
+@example(("w4a16", 16, 512, 4096, torch.float32, 17))       # streaming kernel, K split
+@example(("w4a16", 32, 3072, 12288, torch.bfloat16, 18))    # streaming kernel, 32 rows
+@example(("mx", 4096, 4296, 512, torch.bfloat16, 19))       # MXFP4 mixed plan
+@example(("mx", 2048, 2048, 2048, torch.float32, 20))       # MXFP4 128x128 tiles
+@example(("mx", 8192, 1024, 1024, torch.bfloat16, 21))      # MXFP4 256x256 tiles
+def test_gemm_shapes_against_oracle(case):
+    mode, M, N, K, out_dtype, seed = case
+    if mode == "w4a4_b64" and K % 64:
+        return
+    say(f"[gemm property] {mode} M={M} N={N} K={K} out={out_dtype} seed={seed}")
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 24), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
+    xo, wo = np_x(x), np_x(w)
+    if mode == "mx":
+        a, asc = nv.nvfp4_mx_quantize(x.to(DEV))
+        b, bs = nv.nvfp4_mx_quantize(w.to(DEV))
+        y = nv.nvfp4_mx_gemm(a, asc, b, bs, out_dtype)
+        torch.cuda.synchronize()
+        ap, as_ = oracle.mx_quantize(np.ascontiguousarray(xo[rows]))
+        bp_, bs_ = oracle.mx_quantize(np.ascontiguousarray(wo[cols]))
+        A, _ = oracle.mx_dequantize(ap, as_)
+        B, _ = oracle.mx_dequantize(bp_, bs_)
+    else:
+        bb = 64 if mode == "w4a4_b64" else (32 if mode == "w4a4_b32" else 16)
+        wp, ws, wS = nv.nvfp4_quantize(w.to(DEV), block_size=bb)
+        bp = nv.nvfp4_prepack_weight(wp, ws)
+        SB = oracle.tensor_scale(wo)
+        bo_p, bo_s, _ = oracle.quantize(np.ascontiguousarray(wo[cols]), S=SB, block=bb)
+        B, _ = oracle.dequantize(bo_p, bo_s, SB)
+        if mode == "w4a16":
+            y = nv.nvfp4_gemm(nv.W4A16, x.to(DEV), None, None, bp, wS, N, K, out_dtype)
+            A = oracle.bf16_to_f32(xo[rows])
+        else:
+            pa, sa, Sa = nv.nvfp4_quantize(x.to(DEV), block_size=bb)
+            y = nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bp, wS, N, K, out_dtype)
+            SA = oracle.tensor_scale(xo)
+            ap, as_, _ = oracle.quantize(np.ascontiguousarray(xo[rows]), S=SA, block=bb)
+            A, _ = oracle.dequantize(ap, as_, SA)
+        torch.cuda.synchronize()
+    Y, R = oracle.gemm(A, B)
+    Yg = y.float().cpu().numpy()[np.ix_(rows, cols)]
+    check_gemm(Yg, Y, R, out_dtype == torch.bfloat16, f"{mode} {M}x{N}x{K}")
