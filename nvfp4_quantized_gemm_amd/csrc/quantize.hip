@@ -11,9 +11,9 @@
 // 16-value block combine their maxima with cross-lane swaps, every lane derives the block's scale
 // byte and encodes its own values, lanes store their 4 (bf16) or 2 (fp32) code bytes contiguously
 // and the first lane of each block stores the scale byte.  Each lane keeps four segments' loads in
-// flight; the input is read with streaming (non-temporal) loads, its last use.  Dynamic mode runs k_amax first (same mapping, per-workgroup partial maxima, no atomics,
-// deterministic); every quantize workgroup reduces those partials itself and derives
-// S = RN32(amax / 2688).
+// flight; a large input is read with streaming (non-temporal) loads, its last use.  Dynamic mode
+// runs k_amax first (same mapping, per-workgroup partial maxima, no atomics, deterministic); every
+// quantize workgroup reduces those partials itself and derives S = RN32(amax / 2688).
 //
 // Exactness (all fast paths bracket the exact real quotient and fall back when unsure):
 //  * Block scale.  With c = 1/(6 S) (fp64, once per workgroup), rl = RN32(amax RN32(c (1 - 2^-20)))
@@ -36,6 +36,8 @@
 //    common, so this path must be cheap.)  Outside the bracket's range of S a full exact path
 //    runs: seven per-block fp32 thresholds U_k from the exact fp64 boundaries by directed
 //    rounding, code = #{k : |v| >= U_k}.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "quant_core.hpp"
@@ -43,11 +45,13 @@
 namespace nvfp4 {
 
 constexpr int kSegsPerLane = 4;  // segments in flight per lane
-// Streaming (non-temporal) accesses: the input is read with them by both passes (faster from HBM,
-// also when the encode pass re-reads it); the NVFP4 output is stored normally so that the GEMM
-// that reads it next finds it in the caches; the fake-quantization output is streamed.
-constexpr bool kAmaxNT = true;
-constexpr bool kQuantNT = true;
+// Streaming (non-temporal) accesses: a large input is read with them by both passes (faster from
+// HBM, also when the encode pass re-reads it); an input of at most kCachedInput bytes is read with
+// ordinary loads, so that the encode pass finds what the amax pass read in the last-level cache
+// (9.4 MB: 9.7 -> 9.5 us; 37.7 MB followed by its GEMM: 86.6 -> 83.4 us; 805 MB: 322 -> 357 us,
+// so not there).  Fake quantization always streams.  The NVFP4 output is stored normally so that
+// the GEMM that reads it next finds it in the caches; the fake-quantization output is streamed.
+constexpr uint64_t kCachedInput = 64ull << 20;
 constexpr bool kOutNT = false;
 constexpr bool kFakeOutNT = true;
 
@@ -97,7 +101,7 @@ __device__ __forceinline__ void store_fake(uint32_t codes, uint32_t byte, float 
 
 // ---- dynamic amax: per-workgroup partial maxima ------------------------------------------------------
 
-template <int DT, bool DENSE>
+template <int DT, bool DENSE, bool NT>
 __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                               FastDiv bpr, float *__restrict__ partial) {
   using In = SegIn<DT>;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;  // a repeated segment does not change the maximum
-      In::unpack(In::template raw<kAmaxNT>(x, Map::template offset<DENSE>(g, bpr, ld)), v[u]);
+      In::unpack(In::template raw<NT>(x, Map::template offset<DENSE>(g, bpr, ld)), v[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
 // YT < 0: write the NVFP4 tensor (packed codes + scale bytes).  YT = 0 / 1: fake quantization,
 // write dequantize(quantize(x)) as fp32 / bf16 into y [.][ld_y] instead (one pass, same values as
 // the two calls).
-template <int DT, bool DYNAMIC, bool DENSE, int YT, int BLK>
+template <int DT, bool DYNAMIC, bool DENSE, int YT, int BLK, bool NT>
 __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
                                                   FastDiv bpr, uint8_t *__restrict__ packed,
                                                   uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
     for (int u = 0; u < U; ++u) {
       uint64_t g = t * (64 * U) + u * 64 + lane;
       g = g < nseg ? g : nseg - 1;
-      r[u] = In::template raw<kQuantNT>(x, Map::template offset<DENSE>(g, bpr, ld));
+      r[u] = In::template raw<NT>(x, Map::template offset<DENSE>(g, bpr, ld));
     }
   };
   uint64_t t = blockIdx.x * 4ull + (threadIdx.x >> 6);
@@ -247,14 +251,23 @@ static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr16
   // partials); the others widen it on large tensors
   const bool wide = (!dynamic || YT >= 0) && grid_for(nseg, 1 << 30) > 4 * kQuantizeMaxGrid;
   const int gq = grid_for(nseg, wide ? kQuantizeWideGrid : kQuantizeMaxGrid);
-  if (dynamic) {
-    const int ga = grid_for(nseg, kAmaxPartials);
-    k_amax<DT, DENSE><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr16, partial);
-    k_quantize<DT, true, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
-                                                                 partial, ga, y, ld_y);
+  auto run = [&](auto nt_tag) {
+    constexpr bool NT = decltype(nt_tag)::value;
+    if (dynamic) {
+      const int ga = grid_for(nseg, kAmaxPartials);
+      k_amax<DT, DENSE, NT><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr16, partial);
+      k_quantize<DT, true, DENSE, YT, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales,
+                                                                       tensor_scale, partial, ga, y, ld_y);
+    } else {
+      k_quantize<DT, false, DENSE, YT, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales,
+                                                                        tensor_scale, nullptr, 0, y, ld_y);
+    }
+  };
+  if constexpr (YT >= 0) {
+    run(std::true_type{});
   } else {
-    k_quantize<DT, false, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
-                                                                  nullptr, 0, y, ld_y);
+    if (nseg * 16ull > kCachedInput) run(std::true_type{});
+    else run(std::false_type{});
   }
 }
 
