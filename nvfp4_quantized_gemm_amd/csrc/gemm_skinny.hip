@@ -1,4 +1,4 @@
-// Weight-only NVFP4 GEMM for few activation rows (W4A16, M <= 32): Y = A B^T with A bf16 [M][K]
+// Weight-only NVFP4 GEMM for few activation rows (W4A16, M <= 64): Y = A B^T with A bf16 [M][K]
 // and B an NVFP4 weight in the prepacked layout [NVFP4-DiT page, Methodology section 3; vllm-omni
 // NVFP4 RFC, Open Question 1: weight-only NVFP4].  With M this small the call streams the packed
 // weight once (0.5625 B per weight element) and is bound by HBM bandwidth, not by matrix math.
@@ -13,9 +13,10 @@
 //
 // Activations: in the MFMA operand order every lane holds a different row, so loading them in that
 // order touches 64 cache lines per instruction.  Instead each wave copies its chunk of the first
-// MR rows (MR = M rounded up to 4, 8, 16 or 32; 256 bytes per row) straight into a wave-private
-// LDS ring with row-contiguous 16-byte DMAs (16 lanes per row), L chunks ahead (L = 3, 3, 2, 1 by
-// MR, which keeps two workgroups of 8 waves per CU), and reads the operand order back from there.
+// MR rows (MR = M rounded up to 4, 8, 16, 32 or 64; 256 bytes per row) straight into a
+// wave-private LDS ring with row-contiguous 16-byte DMAs (16 lanes per row), L chunks ahead (L = 3,
+// 3, 2, 1, 1 by MR, which keeps two workgroups of 8 waves, or of 4 waves for 64 rows, per CU), and
+// reads the operand order back from there; 64 rows are two MFMA column operands of 32 rows.
 // The 16-byte pieces of row r are stored XOR-swizzled by r % 16, so that the 16 lanes of each read
 // pass hit 16 different bank groups.
 // The waves' accumulators are added in LDS in wave order (deterministic).  With S = 1 (wide N)
@@ -46,17 +47,20 @@ __device__ __forceinline__ bf16x8 dequant_b(uint32_t codes, float e) {
 }
 
 // Activation ring of one wave: L slots of one chunk of MR rows each; MR / 4 DMAs fill a slot.
+// MR = 64 holds two groups of 32 rows, each its own MFMA column operand.
 template <int MR>
 struct SkinnyA {
-  static_assert(MR == 4 || MR == 8 || MR == 16 || MR == 32, "row classes");
+  static_assert(MR == 4 || MR == 8 || MR == 16 || MR == 32 || MR == 64, "row classes");
   static constexpr int kL = (MR <= 8) ? 3 : (MR == 16 ? 2 : 1);
   static constexpr int kSlot = MR * 256;
   static constexpr int kDma = MR / 4;
+  static constexpr int kGroups = MR > 32 ? MR / 32 : 1;
 };
 
 template <int NW, int MR>
 constexpr int skinny_lds_bytes() {
-  constexpr int ring = NW * SkinnyA<MR>::kL * SkinnyA<MR>::kSlot, red = NW * 16 * 64 * 4;
+  constexpr int ring = NW * SkinnyA<MR>::kL * SkinnyA<MR>::kSlot;
+  constexpr int red = NW * SkinnyA<MR>::kGroups * 16 * 64 * 4;
   return ring > red ? ring : red;
 }
 
@@ -73,14 +77,16 @@ __device__ __forceinline__ void issue_order() {
 
 }  // namespace
 
+// waves per SIMD: 1.5 workgroups per CU of 8 or 16 waves need 4; the 64-row class runs 4-wave
+// workgroups two per CU and needs the registers of a second row group
 template <int OUT, int NW, int MR>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_skinny(const uint16_t *__restrict__ a, int64_t lda,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MR > 32 ? 2 : 4))) void k_gemm_skinny(const uint16_t *__restrict__ a, int64_t lda,
                                                          const uint8_t *__restrict__ bp,
                                                          const float *__restrict__ b_ts, int M, int N, int K,
                                                          void *__restrict__ c, int64_t ldc, int splits,
                                                          float *__restrict__ partial) {
   using SA = SkinnyA<MR>;
-  constexpr int L = SA::kL;
+  constexpr int L = SA::kL, RG = SA::kGroups;
   constexpr int NB = 3;            // vector-memory operations of one chunk's weight loads
   constexpr int NA = SA::kDma;     // ... and of one chunk's activation DMAs
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -94,7 +100,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const uint8_t *bcode = bp + (uint64_t)u * (uint64_t)Kc * 2048ull;
   const uint8_t *bscale = bp + scale_region + (uint64_t)u * (uint64_t)Kc * 256ull;
   const uint32_t lcode = (uint32_t)lane * 16u, lscale = (uint32_t)lane * 4u;
-  const bool has_row = r < M;
 
   // DMA q of a chunk: lane l takes row 4 q + l / 16 (rows past M re-read row M - 1) and lands at
   // LDS unit 64 q + l of the slot, i.e. row-major 256-byte rows holding piece (l % 16) ^ (row % 16).
@@ -117,11 +122,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int nw = (kb + wave < ke) ? (ke - kb - wave + NW - 1) / NW : 0;
   auto chunk_of = [&](int i) { return kb + wave + i * NW; };
 
-  f32x16 acc0, acc1;
+  // one row group: two accumulators alternate between the steps; two row groups: one each, the
+  // groups alternating within a step (either way no MFMA waits on the one before it)
+  f32x16 acc[2];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    acc0[v] = 0.0f;
-    acc1[v] = 0.0f;
+    acc[0][v] = 0.0f;
+    acc[1][v] = 0.0f;
   }
   // Issue order, chunk i: activation DMAs of chunk i + L into the slot chunk i has just read, then
   // weight loads of chunk i + 3 into register slot i % 3 (the loop is unrolled by 3 so slots never
@@ -169,9 +176,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       asm volatile("" : "+v"(ln));
       const int rrow = ln & 31 & (MR - 1), y = (8 * (ln >> 5)) ^ (rrow & 15);
       const uint8_t *rd = aring + sl * SA::kSlot + rrow * 256;
-      u32x4 av[8];
+      u32x4 av[RG][8];  // group g: rows 32 g + r, 32 rows = 8 KB further in the slot
 #pragma unroll
-      for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const u32x4 *>(rd + ((y ^ s) << 4));
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) av[g][s] = *reinterpret_cast<const u32x4 *>(rd + g * 8192 + ((y ^ s) << 4));
       // the slot is refilled next: its reads must have completed
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (i + L < nw) issue_a(i + L, sl);
@@ -182,9 +191,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8 bf = dequant_b(b[J].code[s >> 2][s & 3], e[s >> 1]);
-        const bf16x8 af = __builtin_bit_cast(bf16x8, av[s]);
-        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc1, 0, 0, 0);
-        else acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc0, 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          const int k = (RG == 1) ? (s & 1) : g;
+          acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, __builtin_bit_cast(bf16x8, av[g][s]), acc[k], 0, 0, 0);
+        }
       }
       issue_order();
       if (i + 3 < nw) load_b(chunk_of(i + 3), b[J]);
@@ -201,65 +212,74 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     if (i0 + 1 < nw) body(i0 + 1, std::integral_constant<int, 1>{});
     wait_vmcnt<0>();  // every DMA has landed before the LDS is reused
   }
+  // wave w < 4 finishes column group w of row group g: columns n = 32 u + 8 w + 4 h + j, row
+  // m = 32 g + r; the waves' partial sums are added in wave order (deterministic)
+  auto store_rows = [&](float (*red)[RG][16][64], int g) {
+    float out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * wave + j;
+      float sum = red[0][g][v][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][g][v][lane];
+      out[j] = sum;
+    }
+    const int m = 32 * g + r;
+    if (m >= M) return;
+    const int n = 32 * u + 8 * wave + 4 * h;
+    if (OUT == 2 || splits > 1) {
+      // unscaled fp32 partial; the split-K reduction sums the splits in order, scales and converts
+      // (OUT 2, NVFP4 output: always, the reduction pass requantizes)
+      float *dst = partial + (int64_t)split * M * N + (int64_t)m * N + n;
+      if (n + 3 < N && (N % 4) == 0) {
+        const f32x4 o = {out[0], out[1], out[2], out[3]};
+        *reinterpret_cast<f32x4 *>(dst) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) dst[j] = out[j];
+      }
+      return;
+    }
+    const float sb = *b_ts;
+    if (OUT == 0) {
+      float *dst = static_cast<float *>(c) + (int64_t)m * ldc + n;
+      if (n + 3 < N && (ldc % 4) == 0) {
+        const f32x4 o = {out[0] * sb, out[1] * sb, out[2] * sb, out[3] * sb};
+        *reinterpret_cast<f32x4 *>(dst) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) dst[j] = out[j] * sb;
+      }
+    } else {
+      __bf16 *dst = static_cast<__bf16 *>(c) + (int64_t)m * ldc + n;
+      if (n + 3 < N && (ldc % 4) == 0) {
+        const bf16x2 h0 = {(__bf16)(out[0] * sb), (__bf16)(out[1] * sb)};
+        const bf16x2 h1 = {(__bf16)(out[2] * sb), (__bf16)(out[3] * sb)};
+        const u32x2 o = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+        *reinterpret_cast<u32x2 *>(dst) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) dst[j] = (__bf16)(out[j] * sb);
+      }
+    }
+  };
   // the reduction below reuses the LDS of the activation rings
   __syncthreads();
-  float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(smem);
+  float(*red)[RG][16][64] = reinterpret_cast<float(*)[RG][16][64]>(smem);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) red[wave][v][lane] = acc0[v] + acc1[v];
+  for (int v = 0; v < 16; ++v) {
+    if (RG == 1) red[wave][0][v][lane] = acc[0][v] + acc[1][v];
+    else
+#pragma unroll
+      for (int g = 0; g < RG; ++g) red[wave][g][v][lane] = acc[g][v];
+  }
   __syncthreads();
   if (wave >= 4) return;
-
-  // wave w < 4 finishes column group g = w: columns n = 32 u + 8 w + 4 h + j, row m = r; the
-  // waves' partial sums are added in wave order (deterministic)
-  float out[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int v = 4 * wave + j;
-    float sum = red[0][v][lane];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) sum += red[w][v][lane];
-    out[j] = sum;
-  }
-  if (!has_row) return;
-  const int n = 32 * u + 8 * wave + 4 * h;
-  if (OUT == 2 || splits > 1) {
-    // unscaled fp32 partial; the split-K reduction sums the splits in order, scales and converts
-    // (OUT 2, NVFP4 output: always, the reduction pass requantizes)
-    float *dst = partial + (int64_t)split * M * N + (int64_t)r * N + n;
-    if (n + 3 < N && (N % 4) == 0) {
-      const f32x4 o = {out[0], out[1], out[2], out[3]};
-      *reinterpret_cast<f32x4 *>(dst) = o;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) dst[j] = out[j];
-    }
-    return;
-  }
-  const float sb = *b_ts;
-  if (OUT == 0) {
-    float *dst = static_cast<float *>(c) + (int64_t)r * ldc + n;
-    if (n + 3 < N && (ldc % 4) == 0) {
-      const f32x4 o = {out[0] * sb, out[1] * sb, out[2] * sb, out[3] * sb};
-      *reinterpret_cast<f32x4 *>(dst) = o;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) dst[j] = out[j] * sb;
-    }
-  } else {
-    __bf16 *dst = static_cast<__bf16 *>(c) + (int64_t)r * ldc + n;
-    if (n + 3 < N && (ldc % 4) == 0) {
-      const bf16x2 h0 = {(__bf16)(out[0] * sb), (__bf16)(out[1] * sb)};
-      const bf16x2 h1 = {(__bf16)(out[2] * sb), (__bf16)(out[3] * sb)};
-      const u32x2 o = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
-      *reinterpret_cast<u32x2 *>(dst) = o;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < N) dst[j] = (__bf16)(out[j] * sb);
-    }
-  }
+  for (int g = 0; g < RG; ++g) store_rows(red, g);
 }
 
 template <int OUT, int NW, int MR>
@@ -289,6 +309,9 @@ static hipError_t launch_skinny_rows(const GemmArgs &g, int splits, float *parti
 
 template <int OUT>
 static hipError_t launch_skinny_out(const GemmArgs &g, int nw, int splits, float *partial, hipStream_t stream) {
+  // 33..64 rows: two row groups, 4-wave workgroups (the 16 KB activation slot of 8 waves would
+  // leave one workgroup per CU)
+  if (g.M > 32) return launch_skinny_cfg<OUT, 4, 64>(g, splits, partial, stream);
   if (nw >= 16) return launch_skinny_rows<OUT, 16>(g, splits, partial, stream);
   if (nw >= 8) return launch_skinny_rows<OUT, 8>(g, splits, partial, stream);
   return launch_skinny_rows<OUT, 4>(g, splits, partial, stream);

@@ -76,7 +76,7 @@ size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 
 // W4A16 with M <= kSkinnyMaxM: streaming kernel over the prepacked weight (gemm_skinny.hip)
-constexpr int kSkinnyMaxM = 32;
+constexpr int kSkinnyMaxM = 64;
 hipError_t launch_gemm_skinny(const GemmArgs &g, int waves, int splits, float *partial, hipStream_t stream);
 
 // C = (sum of the splits' fp32 partials [splits][M][N], in order) * (a_ts ? *a_ts : 1) *

@@ -51,6 +51,7 @@ def gemm_case(draw):
 @example(("w4a16", 300, 12288, 3072, torch.float32, 16))    # 128x256 W4A16 tiles
 @example(("w4a16", 16, 512, 4096, torch.float32, 17))       # streaming kernel, K split
 @example(("w4a16", 32, 3072, 12288, torch.bfloat16, 18))    # streaming kernel, 32 rows
+@example(("w4a16", 57, 12288, 3072, torch.bfloat16, 22))    # streaming kernel, two row groups
 @example(("mx", 4096, 4296, 512, torch.bfloat16, 19))       # MXFP4 mixed plan
 @example(("mx", 2048, 2048, 2048, torch.float32, 20))       # MXFP4 128x128 tiles
 @example(("mx", 8192, 1024, 1024, torch.bfloat16, 21))      # MXFP4 256x256 tiles

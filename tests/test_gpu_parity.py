@@ -382,6 +382,8 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
                                    # each activation row class of the streaming kernel (4, 8, 16, 32 rows),
                                    # full and partly filled
                                    (4, 520, 1152), (9, 300, 1152), (17, 1000, 2048), (32, 4096, 3072),
+                                   # two row groups (33..64 rows)
+                                   (33, 1000, 2048), (48, 130, 1152), (64, 4096, 3072),
                                    # tiled kernel with K split
                                    (200, 520, 2048),
                                    # 256-row tiles (half-chunk stages): ragged M and N, K split, 9 chunks
@@ -393,7 +395,7 @@ def test_gemm_w4a16_ragged(M, N, K):
     run_w4a16(a, w, torch.float32)
 
 
-@pytest.mark.parametrize("M", [1, 9, 17, 32, 300])
+@pytest.mark.parametrize("M", [1, 9, 17, 32, 50, 300])
 def test_gemm_w4a16_strided_activation(M):
     """A row-strided activation view (lda = K + 64, the padding holds 1e30 and must be ignored):
     streaming kernel for each row class, tiled kernel for M = 300."""
