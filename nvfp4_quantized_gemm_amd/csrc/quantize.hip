@@ -48,10 +48,10 @@ constexpr int kSegsPerLane = 4;  // segments in flight per lane
 // Streaming (non-temporal) accesses: a large input is read with them by both passes (faster from
 // HBM, also when the encode pass re-reads it); an input of at most kCachedInput bytes is read with
 // ordinary loads, so that the encode pass finds what the amax pass read in the last-level cache
-// (9.4 MB: 9.7 -> 9.5 us; 37.7 MB followed by its GEMM: 86.6 -> 83.4 us; 805 MB: 322 -> 357 us,
-// so not there).  Fake quantization always streams.  The NVFP4 output is stored normally so that
+// (9.4 MB: 9.7 -> 9.5 us; 37.7 MB followed by its GEMM: 86.6 -> 83.4 us; 63 MB alone: 30.8 ->
+// 32.1 us; 805 MB: 322 -> 357 us, so not there).  Fake quantization always streams.  The NVFP4 output is stored normally so that
 // the GEMM that reads it next finds it in the caches; the fake-quantization output is streamed.
-constexpr uint64_t kCachedInput = 64ull << 20;
+constexpr uint64_t kCachedInput = 48ull << 20;
 constexpr bool kOutNT = false;
 constexpr bool kFakeOutNT = true;
 
