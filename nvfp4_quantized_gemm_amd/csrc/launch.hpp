@@ -6,10 +6,11 @@
 namespace nvfp4 {
 
 constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pass (= partials)
-// Grid caps (grid-stride beyond).  The quantize kernel runs 2048 workgroups, all resident (8 per
-// CU), each prefetching its next tile; passes that write more than they read (static
-// quantization and fake quantization of large tensors) measured faster with 16384.  The
-// dequantize kernel, write-dominated too, runs one workgroup per four tiles up to a large cap.
+// Grid caps (grid-stride beyond).  The quantize kernel runs at most 2048 workgroups (its registers
+// allow four or five per CU at once), each prefetching its next tile; passes that write more than
+// they read (static quantization and fake quantization of large tensors) measured faster with
+// 16384.  The dequantize kernel, write-dominated too, runs one workgroup per four tiles up to a
+// large cap.
 constexpr int kQuantizeMaxGrid = 2048;
 constexpr int kQuantizeWideGrid = 16384;
 constexpr int kDequantizeMaxGrid = 1 << 20;
