@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 typedef enum {
   NVFP4_OK = 0,
@@ -158,11 +158,19 @@ nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, 
  *                  a_scales and a_tensor_scale must be NULL.
  *   b_prepacked    weight from nvfp4_prepack_weight(N, K); b_tensor_scale its device fp32 S_B.
  *   c              device, [M][ldc] of c_dtype (fp32 or bf16), ldc >= N, base 16-byte aligned.
- *   workspace      device scratch of nvfp4_gemm_workspace_bytes(mode, M, N, K) bytes (may be NULL
- *                  when that is 0), 16-byte aligned; contents need no initialization.
+ *   workspace      device scratch of nvfp4_gemm_workspace_bytes_ld(mode, M, N, K, lda) bytes (may
+ *                  be NULL when that is 0), 16-byte aligned; contents need no initialization.  The
+ *                  activation's row pitch is part of the plan (a W4A4 lda that is not a multiple of
+ *                  128, for one, selects another kernel), so the query takes it;
+ *                  nvfp4_gemm_workspace_bytes(mode, M, N, K) is the same query with lda == K.  A
+ *                  workspace smaller than the query for the call's own lda returns
+ *                  NVFP4_ERR_WORKSPACE and launches nothing.
+ *   Extents: M, N < 2^30, K < 2^30, N * K and M * N <= 2^40, M * lda <= 2^40 (else
+ *   NVFP4_ERR_SHAPE; the queries return 0 for such arguments).
  *   M == 0 or N == 0 (an empty output) is valid and touches nothing; the pointers may be NULL.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
+size_t nvfp4_gemm_workspace_bytes_ld(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales, const float *a_tensor_scale,
                           const void *b_prepacked, const float *b_tensor_scale, int64_t M, int64_t N, int64_t K,
                           int64_t lda, void *c, nvfp4_dtype_t c_dtype, int64_t ldc, void *workspace,
@@ -222,12 +230,15 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
  *   out_packed     device [M][N/2], 16-byte aligned.   out_scales  device [M][N/16].
  *   y              NULL, or device fp32 [M][ld_y] (ld_y >= N, ld_y % 4 == 0, 16-byte aligned) that
  *                  also receives the fp32 values that were quantized.
- *   workspace      nvfp4_gemm_requant_workspace_bytes(mode, M, N, K) bytes, 16-byte aligned.
+ *   workspace      nvfp4_gemm_requant_workspace_bytes_ld(mode, M, N, K, lda) bytes, 16-byte aligned
+ *                  (may be NULL when that is 0); nvfp4_gemm_requant_workspace_bytes(mode, M, N, K) is
+ *                  the same query with lda == K.  A shorter workspace returns NVFP4_ERR_WORKSPACE.
  *   M == 0 or N == 0 is valid and touches nothing.
  * ------------------------------------------------------------------------------------------- */
 typedef enum { NVFP4_ACT_NONE = 0, NVFP4_ACT_GELU_TANH = 1 } nvfp4_act_t;
 
 size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
+size_t nvfp4_gemm_requant_workspace_bytes_ld(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 nvfp4_status_t nvfp4_gemm_requant(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
                                   const float *a_tensor_scale, const void *b_prepacked, const float *b_tensor_scale,
                                   int64_t M, int64_t N, int64_t K, int64_t lda, const float *bias, nvfp4_act_t act,

@@ -39,8 +39,8 @@ EXPORTED = (
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_dequantize", "nvfp4_fake_quantize",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
-    "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
-    "nvfp4_gemm_requant_workspace_bytes", "nvfp4_gemm_requant",
+    "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_workspace_bytes_ld", "nvfp4_gemm",
+    "nvfp4_gemm_requant_workspace_bytes", "nvfp4_gemm_requant_workspace_bytes_ld", "nvfp4_gemm_requant",
     "nvfp4_quantize_bs", "nvfp4_dequantize_bs", "nvfp4_fake_quantize_bs", "nvfp4_prepack_weight_bs",
     "nvfp4_unpack_weight_bs", "nvfp4_gemm_bs", "nvfp4_gemm_requant_bs",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
@@ -85,10 +85,14 @@ def lib():
     L.nvfp4_unpack_weight.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     L.nvfp4_gemm_workspace_bytes.restype = _sz
     L.nvfp4_gemm_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
+    L.nvfp4_gemm_workspace_bytes_ld.restype = _sz
+    L.nvfp4_gemm_workspace_bytes_ld.argtypes = [_i, _i64, _i64, _i64, _i64]
     L.nvfp4_gemm.restype = _i
     L.nvfp4_gemm.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _i64, _vp, _sz, _vp]
     L.nvfp4_gemm_requant_workspace_bytes.restype = _sz
     L.nvfp4_gemm_requant_workspace_bytes.argtypes = [_i, _i64, _i64, _i64]
+    L.nvfp4_gemm_requant_workspace_bytes_ld.restype = _sz
+    L.nvfp4_gemm_requant_workspace_bytes_ld.argtypes = [_i, _i64, _i64, _i64, _i64]
     L.nvfp4_gemm_requant.restype = _i
     L.nvfp4_gemm_requant.argtypes = [_i, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i, _vp, _vp, _vp,
                                      _vp, _i64, _vp, _sz, _vp]
@@ -286,27 +290,40 @@ def nvfp4_unpack_weight(prepacked: torch.Tensor, N: int, K: int, *, block_size: 
 
 # ---- GEMM -------------------------------------------------------------------------------------------
 
-def nvfp4_gemm_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
-    return int(lib().nvfp4_gemm_workspace_bytes(mode, M, N, K))
+def nvfp4_gemm_workspace_bytes(mode: int, M: int, N: int, K: int, lda: int | None = None) -> int:
+    """Workspace bytes of nvfp4_gemm for an activation with row pitch lda (elements; K when None)."""
+    return int(lib().nvfp4_gemm_workspace_bytes_ld(mode, M, N, K, K if lda is None else lda))
+
+
+def _activation_pitch(mode: int, a: torch.Tensor, a_scales, a_block_size):
+    """(lda in elements, W4A4 activation block size) of a GEMM's A operand.  W4A4: a is packed codes
+    [M, K/2] (a row-strided view is allowed: lda = 2 * its row stride) and a_scales the matching
+    [M, K/block] view of [M, lda/block] bytes; the block size is a_block_size, else lda over the scale
+    tensor's row stride.  W4A16: a is bf16 [M, K] with unit stride along K."""
+    if mode != W4A4:
+        _, _, lda = _rows(a, "a")
+        return lda, 16
+    lda = a.stride(0) * 2
+    if a_block_size is not None:
+        return lda, int(a_block_size)
+    if a_scales is not None and a_scales.dim() == 2 and a_scales.shape[0] >= 1 and a_scales.stride(0) > 0:
+        return lda, lda // a_scales.stride(0)
+    return lda, _block_of(lda, a_scales)
 
 
 def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked: torch.Tensor,
                b_tensor_scale: torch.Tensor, N: int, K: int, out_dtype: torch.dtype = torch.bfloat16, *,
-               out=None, workspace=None, stream=None) -> torch.Tensor:
+               out=None, workspace=None, a_block_size: int | None = None, stream=None) -> torch.Tensor:
     """Y = A B^T.  W4A4: a = packed u8 [M, K/2] with a_scales u8 [M, K/block] and a_tensor_scale
-    (from nvfp4_quantize; the block size is read from the shape of a_scales).  W4A16: a = bf16
-    [M, K], a_scales = a_tensor_scale = None."""
+    (from nvfp4_quantize; both may be row-strided views of wider rows; the block size is
+    a_block_size, else read from the scales' layout).  W4A16: a = bf16 [M, K], a_scales =
+    a_tensor_scale = None."""
     M = a.shape[0]
-    if mode == W4A4:
-        lda = a.stride(0) * 2
-        ablk = _block_of(lda, a_scales)
-    else:
-        _, _, lda = _rows(a, "a")
-        ablk = 16
+    lda, ablk = _activation_pitch(mode, a, a_scales, a_block_size)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     ldc = out.stride(0)
-    ws_need = nvfp4_gemm_workspace_bytes(mode, M, N, K)
+    ws_need = nvfp4_gemm_workspace_bytes(mode, M, N, K, lda)
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -320,30 +337,26 @@ def nvfp4_gemm(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked
 ACT_NONE, ACT_GELU_TANH = 0, 1
 
 
-def nvfp4_gemm_requant_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
-    return int(lib().nvfp4_gemm_requant_workspace_bytes(mode, M, N, K))
+def nvfp4_gemm_requant_workspace_bytes(mode: int, M: int, N: int, K: int, lda: int | None = None) -> int:
+    """Workspace bytes of nvfp4_gemm_requant for an activation with row pitch lda (K when None)."""
+    return int(lib().nvfp4_gemm_requant_workspace_bytes_ld(mode, M, N, K, K if lda is None else lda))
 
 
 def nvfp4_gemm_requant(mode: int, a: torch.Tensor, a_scales, a_tensor_scale, b_prepacked: torch.Tensor,
                        b_tensor_scale: torch.Tensor, N: int, K: int, out_tensor_scale: torch.Tensor, *,
                        bias=None, act: int = ACT_NONE, packed=None, scales=None, y=None, workspace=None,
-                       stream=None):
+                       a_block_size: int | None = None, stream=None):
     """NVFP4 output of A B^T (+ bias) (-> act) under the static out_tensor_scale (device fp32 [1]).
     Operands as nvfp4_gemm.  Returns (packed u8 [M, N/2], scales u8 [M, N/16]); when y (fp32 [M, >= N])
     is given it also receives the fp32 values that were quantized."""
     M = a.shape[0]
-    if mode == W4A4:
-        lda = a.stride(0) * 2
-        ablk = _block_of(lda, a_scales)
-    else:
-        _, _, lda = _rows(a, "a")
-        ablk = 16
+    lda, ablk = _activation_pitch(mode, a, a_scales, a_block_size)
     if packed is None:
         packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
     if scales is None:
         scales = torch.empty((M, N // 16), dtype=torch.uint8, device=a.device)
     ldy = 0 if y is None else y.stride(0)
-    ws_need = nvfp4_gemm_requant_workspace_bytes(mode, M, N, K)
+    ws_need = nvfp4_gemm_requant_workspace_bytes(mode, M, N, K, lda)
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -694,13 +694,9 @@ static hipError_t launch_tiled(const GemmArgs &g, int m_off, int n_off, int m_le
   const int tm = (m_len + BM - 1) / BM, tn = (n_len + BN - 1) / BN;
   auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT, ABLK>;
   const int smem = 3 * Cfg::kStage;
-  static bool configured = false;  // per instantiation
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<bool> configured[kMaxDevices];  // per instantiation and device
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), smem, configured);
+  if (e != hipSuccess) return e;
   kern<<<tm * tn * splits, 256, smem, stream>>>(g.a, g.a_scales, g.a_ts, static_cast<const uint8_t *>(g.b), g.b_ts,
                                                 (int)g.M, (int)g.N, (int)g.K, g.lda, g.c, g.ldc, tm, tn, m_off, n_off,
                                                 splits, partial, g.qo);
@@ -801,13 +797,13 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   return pl;
 }
 
-size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
-  const GemmPlan pl = plan_gemm(mode, M, N, K, K);
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
+  const GemmPlan pl = plan_gemm(mode, M, N, K, lda);
   return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K) {
-  const GemmPlan pl = plan_gemm(mode, M, N, K, K);
+size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
+  const GemmPlan pl = plan_gemm(mode, M, N, K, lda);
   const size_t mn = (size_t)M * (size_t)N * sizeof(float);
   // the generic and skinny kernels produce fp32 first; the reduction pass requantizes
   if (pl.variant == GemmVariant::Generic || pl.variant == GemmVariant::W4A16_Skinny) return (size_t)pl.splits * mn;

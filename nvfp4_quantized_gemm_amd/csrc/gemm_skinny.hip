@@ -285,13 +285,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MR > 32
 template <int OUT, int NW, int MR>
 static hipError_t launch_skinny_cfg(const GemmArgs &g, int splits, float *partial, hipStream_t stream) {
   constexpr int smem = skinny_lds_bytes<NW, MR>();
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_skinny<OUT, NW, MR>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<bool> configured[kMaxDevices];  // per instantiation and device
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(k_gemm_skinny<OUT, NW, MR>), smem, configured);
+  if (e != hipSuccess) return e;
   const int Nu = (int)((g.N + 31) / 32);
   k_gemm_skinny<OUT, NW, MR><<<(unsigned)(Nu * splits), NW * 64, smem, stream>>>(
       static_cast<const uint16_t *>(g.a), g.lda, static_cast<const uint8_t *>(g.b), g.b_ts, (int)g.M, (int)g.N,

@@ -3,7 +3,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
+
+// Per-device, per-kernel one-time setup of the dynamic LDS limit (kernels whose LDS exceeds the
+// default).  `done` is one flag array per kernel instantiation.  Thread-safe: concurrent first
+// calls on a device may both set the attribute, which is idempotent; a flag is only raised after
+// a successful call.  Devices with an index >= kMaxDevices set it on every launch.
+constexpr int kMaxDevices = 64;
+inline hipError_t set_dynamic_lds(const void *kern, int bytes, std::atomic<bool> *done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && slot) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pass (= partials)
 // Grid caps (grid-stride beyond).  The quantize kernel runs at most 2048 workgroups (its registers
@@ -71,9 +89,11 @@ struct GemmArgs {
 };
 
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
-size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+// Workspace of exactly the plan launch_gemm runs for these arguments (the activation's row pitch
+// lda decides between the tiled and the generic kernels, so it is part of the plan).
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 // workspace of the NVFP4-output GEMM: fp32 partials wherever the plan does not end in a tile kernel
-size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+size_t gemm_requant_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K, int64_t lda);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 
 // W4A16 with M <= kSkinnyMaxM: streaming kernel over the prepacked weight (gemm_skinny.hip)

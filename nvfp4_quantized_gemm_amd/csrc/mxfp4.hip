@@ -490,13 +490,9 @@ static hipError_t launch_mx_tiled(const uint8_t *a, const uint8_t *as, const uin
   using Cfg = MxCfg<T, WM, WN, SX>;
   const int tm = (int)((M + T - 1) / T), tn = (int)((N + T - 1) / T);
   constexpr int smem = Cfg::kLds;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_gemm<OUT, T, WM, WN, SX>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static std::atomic<bool> configured[kMaxDevices];  // per instantiation and device
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(k_mx_gemm<OUT, T, WM, WN, SX>), smem, configured);
+  if (e != hipSuccess) return e;
   k_mx_gemm<OUT, T, WM, WN, SX><<<tm * tn, Cfg::kWaves * 64, smem, stream>>>(a, as, b, bs, (int)M, (int)N, (int)K, c,
                                                                             ldc, tm, tn);
   return hipGetLastError();

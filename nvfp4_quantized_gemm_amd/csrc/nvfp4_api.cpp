@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 
 #include "launch.hpp"
@@ -34,18 +35,32 @@ nvfp4_status_t check_bs(int64_t K, int bs) {
 int elem_size(nvfp4_dtype_t t) { return t == NVFP4_F32 ? 4 : 2; }
 bool valid_dtype(int t) { return t == NVFP4_F32 || t == NVFP4_BF16; }
 
-// The current device must be gfx950.  Queried once per device and cached.
+// The current device must be gfx950.  Queried once per device index and cached in atomics
+// (0 unknown, 1 gfx950, 2 another device), so concurrent callers on any devices are race-free;
+// device indices >= kMaxDevices are queried on every call.
 nvfp4_status_t check_device() {
-  static int cached_dev = -1;
-  static bool cached_ok = false;
+  static std::atomic<int8_t> state[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
-  if (dev == cached_dev) return cached_ok ? NVFP4_OK : NVFP4_ERR_DEVICE;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot) {
+    const int8_t s = state[dev].load(std::memory_order_acquire);
+    if (s != 0) return s == 1 ? NVFP4_OK : NVFP4_ERR_DEVICE;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_ERR_HIP;
-  cached_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  cached_dev = dev;
-  return cached_ok ? NVFP4_OK : NVFP4_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (slot) state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  return ok ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+// GEMM sizes beyond the 32-bit row / column / depth indices of the kernels.  K and the activation
+// pitch are bounded too: the launchers pass K as a 32-bit value and A offsets are formed from lda.
+nvfp4_status_t check_gemm_extent(int64_t M, int64_t N, int64_t K, int64_t lda) {
+  if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30) || K >= (1 << 30))
+    return NVFP4_ERR_SHAPE;
+  if (lda > kMaxElems / M) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
 }
 
 nvfp4_status_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
@@ -216,10 +231,15 @@ nvfp4_status_t nvfp4_unpack_weight(const void *prepacked, int64_t N, int64_t K, 
   return nvfp4_unpack_weight_bs(prepacked, N, K, 16, packed, scales, stream);
 }
 
-size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+size_t nvfp4_gemm_workspace_bytes_ld(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return 0;
-  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0) return 0;  // empty calls need no workspace
-  return gemm_workspace_bytes((int)mode, M, N, K);
+  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || lda < K) return 0;  // empty or invalid calls
+  if (check_gemm_extent(M, N, K, lda) != NVFP4_OK) return 0;
+  return gemm_workspace_bytes((int)mode, M, N, K, lda);
+}
+
+size_t nvfp4_gemm_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+  return nvfp4_gemm_workspace_bytes_ld(mode, M, N, K, K);
 }
 
 nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
@@ -237,8 +257,9 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
   if (M == 0 || N == 0) return NVFP4_OK;  // empty output: nothing to read or write
   if (!a || !b_prepacked || !b_tensor_scale || !c) return NVFP4_ERR_NULL;
   if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
-  if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
   if (lda < K || ldc < N) return NVFP4_ERR_STRIDE;
+  st = check_gemm_extent(M, N, K, lda);
+  if (st != NVFP4_OK) return st;
   if (mode == NVFP4_W4A4) {
     if ((lda % a_block_size) != 0) return NVFP4_ERR_STRIDE;  // whole scale blocks per row
     if (!aligned(a, 8) || !aligned(a_scales, 4)) return NVFP4_ERR_ALIGN;
@@ -246,7 +267,7 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
     if (!aligned(a, 16) || ((lda * 2) % 16) != 0) return NVFP4_ERR_ALIGN;
   }
   if (!aligned(b_prepacked, 16) || !aligned(c, 16) || !aligned(b_tensor_scale, 4)) return NVFP4_ERR_ALIGN;
-  const size_t need = nvfp4_gemm_workspace_bytes(mode, M, N, K);
+  const size_t need = nvfp4_gemm_workspace_bytes_ld(mode, M, N, K, lda);  // the plan the launch runs
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
@@ -282,10 +303,15 @@ nvfp4_status_t nvfp4_gemm(nvfp4_mode_t mode, const void *a, const uint8_t *a_sca
 
 // ---- GEMM with NVFP4 output ------------------------------------------------------------------
 
-size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+size_t nvfp4_gemm_requant_workspace_bytes_ld(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   if (mode != NVFP4_W4A4 && mode != NVFP4_W4A16) return 0;
-  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || (N % 16) != 0) return 0;  // empty or invalid calls
-  return gemm_requant_workspace_bytes((int)mode, M, N, K);
+  if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || (N % 16) != 0 || lda < K) return 0;  // empty or invalid
+  if (check_gemm_extent(M, N, K, lda) != NVFP4_OK) return 0;
+  return gemm_requant_workspace_bytes((int)mode, M, N, K, lda);
+}
+
+size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K) {
+  return nvfp4_gemm_requant_workspace_bytes_ld(mode, M, N, K, K);
 }
 
 nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_scales,
@@ -305,8 +331,9 @@ nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uin
   if (!a || !b_prepacked || !b_tensor_scale || !out_tensor_scale || !out_packed || !out_scales)
     return NVFP4_ERR_NULL;
   if (mode == NVFP4_W4A4 && (!a_scales || !a_tensor_scale)) return NVFP4_ERR_NULL;
-  if (N > kMaxElems / K || M > kMaxElems / N || M >= (1 << 30) || N >= (1 << 30)) return NVFP4_ERR_SHAPE;
   if (lda < K) return NVFP4_ERR_STRIDE;
+  st = check_gemm_extent(M, N, K, lda);
+  if (st != NVFP4_OK) return st;
   if (y && (ld_y < N || (ld_y % 4) != 0)) return NVFP4_ERR_STRIDE;
   if (mode == NVFP4_W4A4) {
     if ((lda % a_block_size) != 0) return NVFP4_ERR_STRIDE;  // whole scale blocks per row
@@ -317,7 +344,7 @@ nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uin
   if (!aligned(b_prepacked, 16) || !aligned(b_tensor_scale, 4) || !aligned(out_tensor_scale, 4) ||
       !aligned(out_packed, 16) || (bias && !aligned(bias, 16)) || (y && !aligned(y, 16)))
     return NVFP4_ERR_ALIGN;
-  const size_t need = nvfp4_gemm_requant_workspace_bytes(mode, M, N, K);
+  const size_t need = nvfp4_gemm_requant_workspace_bytes_ld(mode, M, N, K, lda);  // the plan the launch runs
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;

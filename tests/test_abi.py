@@ -38,7 +38,7 @@ def test_exports_every_header_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_abi_version() == 2
     for s in nv.Status:
         assert len(L.nvfp4_status_string(int(s))) > 0
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -171,6 +171,53 @@ def test_gemm_requant_validation(L):
     # empty outputs touch nothing
     assert rq(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, ots=NULL, op=NULL, osc=NULL, M=0) == S.OK
     assert rq(L, a=NULL, asc=NULL, ats=NULL, b=NULL, bts=NULL, ots=NULL, op=NULL, osc=NULL, N=0) == S.OK
+
+
+def test_workspace_queries_follow_the_activation_pitch(L):
+    """The workspace a GEMM call needs is that of the plan its own lda selects: a W4A4 row pitch that
+    is not a multiple of 128 codes runs the generic kernel, whose NVFP4-output form stages fp32
+    values in the workspace.  The entry points check the caller's buffer against that plan and
+    return ERR_WORKSPACE before any device work when it is short (NVFP4-DiT page, Methodology
+    section 3: the packed operands of the next W4A4 product)."""
+    S = nv.Status
+    M, N, K = 300, 272, 384
+    # lda = K and K + 128: 128 x 128 tiles, no partials; K + 16: the generic kernel
+    assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, K) == 0
+    assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, K + 128) == 0
+    assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == M * N * 4
+    assert L.nvfp4_gemm_requant_workspace_bytes(nv.W4A4, M, N, K) == 0
+    # the call with a pitch of 400 codes and no workspace is refused on the host
+    assert rq(L, M=M, N=N, K=K, lda=400) == S.ERR_WORKSPACE
+    assert rq(L, M=M, N=N, K=K, lda=400, ws=P, wsb=M * N * 4 - 1) == S.ERR_WORKSPACE
+    # the bf16 / fp32 output of the generic kernel needs none
+    assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == 0
+    # a split-K plan: two fp32 partials with lda = K or K + 128, none for the generic kernel
+    M, N, K = 512, 512, 4096
+    for ld in (K, K + 128):
+        assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == 2 * M * N * 4
+        assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == 2 * M * N * 4
+    assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == 0
+    assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == M * N * 4
+    assert L.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K) == 2 * M * N * 4
+    assert g(L, M=M, N=N, K=K, lda=K + 128, ldc=N, ws=P, wsb=2 * M * N * 4 - 16) == S.ERR_WORKSPACE
+    # W4A16 rows <= 64 stream unless 32 rows of the pitch pass 2 GiB; the tiled plan then decides
+    lda = 1 << 26
+    assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A16, 16, 3072, 12288, 12288) == \
+        L.nvfp4_gemm_workspace_bytes(nv.W4A16, 16, 3072, 12288)
+    need_tiled = L.nvfp4_gemm_workspace_bytes_ld(nv.W4A16, 16, 3072, 12288, lda)
+    assert need_tiled in (0,) or need_tiled % (16 * 3072 * 4) == 0
+    # a pitch below K is not a call: the queries return 0
+    assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, 64, 64, 128, 112) == 0
+
+
+def test_gemm_extent_bounds(L):
+    """K and the activation pitch are bounded like M and N (the kernels take 32-bit depths)."""
+    S = nv.Status
+    big = 1 << 30
+    assert g(L, M=1, N=16, K=big, lda=big, ldc=16) == S.ERR_SHAPE
+    assert rq(L, M=1, N=16, K=big, lda=big) == S.ERR_SHAPE
+    assert g(L, M=1 << 20, N=64, K=128, lda=1 << 21, ldc=64) == S.ERR_SHAPE   # M * lda > 2^40
+    assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, 1, 16, big, big) == 0
 
 
 def test_empty_tensors_touch_nothing(L):
