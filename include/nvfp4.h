@@ -210,6 +210,24 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
                              void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Quantize without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments, checks
+ * and results as nvfp4_quantize_bs, minus the workspace: the dynamic pass's partial maxima go to a
+ * scratch array the library holds in device memory, 4096 bytes (NVFP4 quantize workspace) per GPU,
+ * kept from the first call on that GPU until the process ends.  Every size nvfp4_quantize_bs
+ * accepts fits it (its workspace query is 4096 bytes for every M, K); a call whose need exceeded
+ * the scratch would return NVFP4_ERR_WORKSPACE and launch nothing.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine); the caller passes inputs and outputs.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (different streams without
+ * ordering between them) race and give undefined results; calls ordered on a stream do not.  No
+ * scratch contents carry from one call to the next (each call writes every partial it reads).
+ * STATIC mode uses no scratch.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                      int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                      nvfp4_scale_mode_t mode, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * GEMM with NVFP4 output (epilogue-fused requantization) [NVFP4-DiT page, Methodology section 3:
  * packed operands for the next W4A4 product, produced on the fly; Definition III.1 for the
  * encoding].  The product is formed exactly as in nvfp4_gemm; in fp32,

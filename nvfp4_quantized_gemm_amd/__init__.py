@@ -44,6 +44,7 @@ EXPORTED = (
     "nvfp4_quantize_bs", "nvfp4_dequantize_bs", "nvfp4_fake_quantize_bs", "nvfp4_prepack_weight_bs",
     "nvfp4_unpack_weight_bs", "nvfp4_gemm_bs", "nvfp4_gemm_requant_bs",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
+    "nvfp4_quantize_noalloc",
 )
 
 _lib = None
@@ -116,6 +117,8 @@ def lib():
     L.nvfp4_mx_dequantize.restype = _i
     L.nvfp4_mx_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _i, _i64, _vp]
     L.nvfp4_mx_gemm.restype = _i
+    L.nvfp4_quantize_noalloc.restype = _i
+    L.nvfp4_quantize_noalloc.argtypes = [_vp, _i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _i, _vp]
     L.nvfp4_mx_gemm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i, _i64, _vp]
     _lib = L
     return L
@@ -191,6 +194,19 @@ def nvfp4_quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, *,
                                  _stream(stream))
     _check(st, "nvfp4_quantize_bs")
     return packed, scales, S
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, tensor_scale: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                           *, static: bool = False, block_size: int = 16, stream=None):
+    """nvfp4_quantize into caller-given outputs with no workspace: the dynamic pass uses the library's
+    own device scratch, so neither this call nor the library allocates anything.  tensor_scale is
+    written (dynamic) or read (static).  Calls that overlap on one GPU race (they share the scratch)."""
+    M, K, ld = _rows(x, "x")
+    st = lib().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x.dtype), M, K, ld, block_size, _ptr(packed),
+                                      _ptr(scales), _ptr(tensor_scale), SCALE_STATIC if static else SCALE_DYNAMIC,
+                                      _stream(stream))
+    _check(st, "nvfp4_quantize_noalloc")
+    return packed, scales, tensor_scale
 
 
 def _block_of(K: int, scales: torch.Tensor) -> int:
@@ -408,7 +424,8 @@ def nvfp4_mx_gemm(a: torch.Tensor, a_scales: torch.Tensor, b: torch.Tensor, b_sc
 __all__ = [
     "Status", "NVFP4Error", "lib", "LIB_PATH", "EXPORTED", "F32", "BF16", "W4A4", "W4A16",
     "SCALE_DYNAMIC", "SCALE_STATIC",
-    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_fake_quantize",
+    "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_dequantize",
+    "nvfp4_fake_quantize",
     "FakeQuantizeSTE", "fake_quantize_ste",
     "nvfp4_prepacked_bytes", "nvfp4_prepack_weight", "nvfp4_unpack_weight",
     "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",

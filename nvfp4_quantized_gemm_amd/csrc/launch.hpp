@@ -36,6 +36,10 @@ constexpr int kDequantizeMaxGrid = 1 << 20;
 // blk: values per E4M3 scale byte along K (16, 32 or 64)
 hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, uint8_t *packed,
                            uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, hipStream_t stream);
+// Library-owned device scratch for the dynamic pass's partial maxima (the no-allocation entry
+// point): kQuantizeScratchBytes per GPU; *ptr receives the current device's address of it.
+constexpr size_t kQuantizeScratchBytes = (size_t)kAmaxPartials * sizeof(float);
+hipError_t quantize_scratch(float **ptr);
 // Fake quantization: y = dequantize(quantize(x)) in one pass (no NVFP4 tensor is written).
 hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, void *y,
                                 int y_dtype, int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,

@@ -93,9 +93,14 @@ size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K) {
   return (size_t)kAmaxPartials * sizeof(float);
 }
 
-nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
-                                 int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
-                                 nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by the quantize entry points (everything but the workspace).
+nvfp4_status_t check_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                              int block_size, const uint8_t *packed, const uint8_t *scales,
+                              const float *tensor_scale, nvfp4_scale_mode_t mode, bool *nothing_to_do) {
+  *nothing_to_do = false;
   if (!tensor_scale) return NVFP4_ERR_NULL;
   if (!valid_dtype(x_dtype)) return NVFP4_ERR_DTYPE;
   if (mode != NVFP4_SCALE_DYNAMIC && mode != NVFP4_SCALE_STATIC) return NVFP4_ERR_MODE;
@@ -104,11 +109,26 @@ nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M
   st = check_bs(K, block_size);
   if (st != NVFP4_OK) return st;
   if (M > 0 && (!x || !packed || !scales)) return NVFP4_ERR_NULL;
-  if (M == 0 && mode == NVFP4_SCALE_STATIC) return NVFP4_OK;  // nothing to read or write
+  if (M == 0 && mode == NVFP4_SCALE_STATIC) {  // nothing to read or write
+    *nothing_to_do = true;
+    return NVFP4_OK;
+  }
   if (ld_x < K) return NVFP4_ERR_STRIDE;
   const int es = elem_size(x_dtype);
   if (!aligned(x, 16) || ((ld_x * es) % 16) != 0 || !aligned(packed, 8) || !aligned(tensor_scale, 4))
     return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                 int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                 nvfp4_scale_mode_t mode, void *workspace, size_t workspace_bytes, void *stream) {
+  bool done = false;
+  nvfp4_status_t st = check_quantize(x, x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale, mode, &done);
+  if (st != NVFP4_OK || done) return st;
   if (mode == NVFP4_SCALE_DYNAMIC) {
     if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
@@ -118,6 +138,26 @@ nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M
   return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale,
                                     mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
                                     static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
+                                      int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                      nvfp4_scale_mode_t mode, void *stream) {
+  bool done = false;
+  nvfp4_status_t st = check_quantize(x, x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale, mode, &done);
+  if (st != NVFP4_OK || done) return st;
+  // the library's scratch must hold what the call needs (the dynamic pass's partial maxima)
+  if (mode == NVFP4_SCALE_DYNAMIC && nvfp4_quantize_workspace_bytes(M, K) > kQuantizeScratchBytes)
+    return NVFP4_ERR_WORKSPACE;
+  st = check_device();
+  if (st != NVFP4_OK) return st;
+  float *partial = nullptr;
+  if (mode == NVFP4_SCALE_DYNAMIC) {
+    st = hip_status(quantize_scratch(&partial));
+    if (st != NVFP4_OK) return st;
+  }
+  return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale,
+                                    mode == NVFP4_SCALE_DYNAMIC, partial, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,

@@ -321,6 +321,35 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t M, int64_t K, int64
   return hipGetLastError();
 }
 
+// ---- library-owned scratch (the no-allocation quantize entry point) ----------------------------------
+// The dynamic pass's per-workgroup partial maxima, for callers that cannot allocate a workspace.
+// Each GPU holds its own copy of this array from the first use until the process ends; every call on
+// a GPU shares it (each call writes every partial it reads before reading it, so nothing needs
+// clearing, and calls that overlap on one GPU race).  In host code the array's name is only a
+// stand-in: its device address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) float scratch[kAmaxPartials];
+static_assert(sizeof(scratch) == kQuantizeScratchBytes, "scratch size");
+static std::atomic<float *> scratch_addr[kMaxDevices];
+
+hipError_t quantize_scratch(float **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float *p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void *q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (q == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float *>(q);
+    scratch_addr[dev].store(p, std::memory_order_release);  // concurrent first calls store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_fake_quantize(const void *x, int dtype, int64_t M, int64_t K, int64_t ld, int blk, void *y,
                                 int y_dtype, int64_t ld_y, float *tensor_scale, bool dynamic, float *partial,
                                 hipStream_t stream) {
