@@ -53,8 +53,11 @@ def parse():
     ap.add_argument("--no-other", action="store_true",
                     help="skip the video-DiT W4A4 and the matrix-bound W4A16 section")
     ap.add_argument("--kernel-probe", action="store_true",
-                    help="only launch the dominant GEMM call and a 256 MiB device copy, --steps times each "
+                    help="only launch one GEMM call (--probe-shape) and a 256 MiB device copy, --steps times each "
                          "(the workload of the rocprofv3 counter passes)")
+    ap.add_argument("--probe-shape", default="fc2", choices=sorted(PROBE_SHAPES),
+                    help="the call --kernel-probe launches: a PixArt block linear (W4A4, bf16 out), the video-DiT "
+                         "qkv linear (W4A4), or the weight-only up projection at M = 256 / 4096 (W4A16)")
     return ap.parse_args()
 
 
@@ -262,6 +265,10 @@ def main():
 
 
 DOMINANT = "fc2"  # the block's longest GEMM call (4608 -> 1152)
+# --kernel-probe shapes: (mode, M, N, K); the PixArt linears use the block's own inputs
+PROBE_SHAPES = {"qkv": None, "proj": None, "fc1": None, "fc2": None,
+                "video_qkv": ("W4A4", 10240, 9216, 3072), "w4a16_up_256": ("W4A16", 256, 12288, 3072),
+                "w4a16_up_4096": ("W4A16", 4096, 12288, 3072)}
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fc2_traffic.json")
 KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp", "epilogue.hpp", "quant_core.hpp")  # the dominant GEMM call's code
@@ -297,12 +304,38 @@ def measured_traffic():
 
 
 def kernel_probe(args, layers, gemm):
-    """Counter-pass workload: the dominant GEMM call, then a plain device copy of COPY_BYTES."""
+    """Counter-pass workload: one GEMM call (--probe-shape), then a plain device copy of COPY_BYTES."""
     import torch
-    L = next(L for L in layers if L["name"] == DOMINANT)
-    print(f"probe: nvfp4_gemm W4A4 {DOMINANT} M={L['M']} N={L['N']} K={L['K']} x {args.steps}", flush=True)
+
+    import nvfp4_quantized_gemm_amd as nv
+    import workloads
+
+    name = args.probe_shape
+    if PROBE_SHAPES[name] is None:
+        L = next(L for L in layers if L["name"] == name)
+        print(f"probe: nvfp4_gemm W4A4 {name} M={L['M']} N={L['N']} K={L['K']} x {args.steps}", flush=True)
+        call = lambda: gemm(L)
+    else:
+        mode, M, N, K = PROBE_SHAPES[name]
+        g = torch.Generator().manual_seed(5)
+        w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16).cuda()
+        wp, ws, wS = nv.nvfp4_quantize(w)
+        bp = nv.nvfp4_prepack_weight(wp, ws)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        if mode == "W4A4":
+            x = workloads.video_activation(M, K, g).cuda()
+            pa, sa, Sa = nv.nvfp4_quantize(x)
+            ws_ = torch.empty(max(1, nv.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K)), dtype=torch.uint8,
+                              device="cuda")
+            call = lambda: nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bp, wS, N, K, torch.bfloat16, out=y, workspace=ws_)
+        else:
+            a = torch.randn(M, K, generator=g).to(torch.bfloat16).cuda()
+            ws_ = torch.empty(max(1, nv.nvfp4_gemm_workspace_bytes(nv.W4A16, M, N, K)), dtype=torch.uint8,
+                              device="cuda")
+            call = lambda: nv.nvfp4_gemm(nv.W4A16, a, None, None, bp, wS, N, K, torch.bfloat16, out=y, workspace=ws_)
+        print(f"probe: nvfp4_gemm {mode} {name} M={M} N={N} K={K} x {args.steps}", flush=True)
     for _ in range(args.steps):
-        gemm(L)
+        call()
     torch.cuda.synchronize()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)

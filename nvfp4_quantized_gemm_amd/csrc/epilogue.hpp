@@ -56,6 +56,19 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
       }
     }
     wave_lds_sync();
+    // A slab wholly inside C (the common case) stores without per-lane bounds checks; the test is
+    // wave-uniform, so interior tiles never execute the ragged-edge code below.
+    const bool interior = vec && (row0 + i * 32 + 31 < M) && (col0 + CW <= N);
+    if (interior) {
+      OutT *pc = C + (int64_t)(row0 + i * 32 + rr) * ldc + (col0 + cq);
+#pragma unroll
+      for (int t = 0; t < 32 / kRowsPerRead; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + (t * kRowsPerRead + rr) * kPitch + cq * ES);
+        store16<NT>(pc + (int64_t)(t * kRowsPerRead) * ldc, v);
+      }
+      wave_lds_sync();  // the next slab overwrites this region
+      continue;
+    }
 #pragma unroll
     for (int t = 0; t < 32 / kRowsPerRead; ++t) {
       const int r = t * kRowsPerRead + rr;
