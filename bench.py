@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per per-kernel timing graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows per linear (0: auto)")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU oracle's row samples (0: 256)")
     ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernel section")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 section")
     ap.add_argument("--no-requant", action="store_true", help="skip the fused-requantization section")
@@ -651,47 +651,119 @@ def other_configs_section(side, stream, reps):
     return res
 
 
+def host_identity():
+    """CPU model name, logical CPUs of the host, and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(layers, rows):
-    """CPU oracle on a bounded sample: per linear, the dynamic tensor scale over the full activation,
-    then quantize + dequantize + fp64-accumulated GEMM for `rows` rows against the full weight
-    (the weight's own quantization is offline on both sides and not timed)."""
+    """The CPU oracle (plain C, OpenMP over rows, fp64-accumulated GEMM) on this machine's host cores,
+    timed with all the threads this job may use and with one thread.  The headline value is the
+    whole PixArt block on all threads (every row of every linear: the activation's tensor scale,
+    quantize, dequantize and the GEMM against the offline-quantized weight).  Alongside: the tiny
+    fp32 linear end to end, single-thread rates on a leading-row sample (extrapolated linearly, and
+    labelled so), the video-DiT linears and the weight-only GEMM on leading-row samples, and the
+    quantize / dequantize rate on a sweep tensor.  `rows` caps the sampled rows (0: 256)."""
     import numpy as np
     import torch
 
     import oracle
+    import workloads
 
-    threads = oracle.default_threads()
-    prep = []
-    for L in layers:
-        w16 = L["w_cpu"].view(torch.int16).numpy().view(np.uint16)
-        bp, bs, bS = oracle.quantize(w16, threads=threads)
-        B, _ = oracle.dequantize(bp, bs, bS, threads=threads)
-        x16 = L["x_cpu"].view(torch.int16).numpy().view(np.uint16)
-        prep.append((x16, B))
-    if rows <= 0:
-        # calibrate on 32 rows of the first linear: aim for roughly 15 s of oracle work in total
-        x16, B = prep[0]
-        t = time.perf_counter()
-        S = oracle.tensor_scale(x16)
-        p, s, _ = oracle.quantize(np.ascontiguousarray(x16[:32]), S=S, threads=threads)
-        A, _ = oracle.dequantize(p, s, S, threads=threads)
-        oracle.gemm(A, B, threads=threads)
-        dt = time.perf_counter() - t
-        rate = 2.0 * 32 * B.shape[0] * B.shape[1] / max(dt, 1e-6)
-        total_per_row = sum(2.0 * Bx.shape[0] * Bx.shape[1] for _, Bx in prep)
-        rows = int(max(16, min(layers[0]["M"], 15.0 * rate / total_per_row)))
-    flops = 0.0
+    host = host_identity()
+    threads = max(1, min(host["usable_cpus"], int(os.environ.get("OMP_NUM_THREADS", host["usable_cpus"]))))
+    srows = rows if rows > 0 else 256
+    bf16 = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+
+    def linear(x, B, nthreads, nrows=None):
+        """tensor scale over all of x, then quantize + dequantize + GEMM for the first nrows rows"""
+        S = oracle.tensor_scale(x)
+        xs = x if nrows is None else np.ascontiguousarray(x[:nrows])
+        p, sc, _ = oracle.quantize(xs, S=S, threads=nthreads)
+        A, _ = oracle.dequantize(p, sc, S, threads=nthreads)
+        oracle.gemm(A, B, threads=nthreads)
+        return 2.0 * xs.shape[0] * B.shape[0] * B.shape[1]
+
+    def weight(w, nthreads):
+        bp, bs, bS = oracle.quantize(w, threads=nthreads)
+        return oracle.dequantize(bp, bs, bS, threads=nthreads)[0]
+
+    res = {"kind": "oracle", "host": host, "threads": threads}
+    # PixArt block (the benchmark's workload): full on all threads; one thread on a row sample
+    prep = [(bf16(L["x_cpu"]), weight(bf16(L["w_cpu"]), threads)) for L in layers]
     t = time.perf_counter()
-    for x16, B in prep:
-        S = oracle.tensor_scale(x16)
-        p, s, _ = oracle.quantize(np.ascontiguousarray(x16[:rows]), S=S, threads=threads)
-        A, _ = oracle.dequantize(p, s, S, threads=threads)
-        oracle.gemm(A, B, threads=threads)
-        flops += 2.0 * rows * B.shape[0] * B.shape[1]
+    flops = sum(linear(x, B, threads) for x, B in prep)
     dt = time.perf_counter() - t
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {layers[0]['M']} rows of every linear (full-activation tensor scale, "
-                      f"quantize, dequantize, fp64-accumulated GEMM); {dt:.1f} s"}
+    value = flops / dt / 1e12
+    t = time.perf_counter()
+    f1 = sum(linear(x, B, 1, srows) for x, B in prep)
+    dt1 = time.perf_counter() - t
+    res["pixart_block"] = {"all_threads_s": round(dt, 3), "all_threads_TFLOPs": round(value, 6),
+                           "one_thread_TFLOPs": round(f1 / dt1 / 1e12, 6),
+                           "one_thread_s_extrapolated": round(dt1 * layers[0]["M"] / srows, 2),
+                           "one_thread_sample": f"first {srows} of {layers[0]['M']} rows of every linear, "
+                                                f"{dt1:.2f} s, extrapolated linearly"}
+    # tiny fp32 linear end to end (weight quantization included): the seconds-scale oracle run
+    x, w = workloads.tiny()
+    for n, key in ((threads, "all_threads_s"), (1, "one_thread_s")):
+        t = time.perf_counter()
+        linear(x.numpy(), weight(w.numpy(), n), n)
+        res.setdefault("tiny_w4a4", {})[key] = round(time.perf_counter() - t, 4)
+    # video-DiT linears and the weight-only GEMM: leading-row samples on all threads, extrapolated
+    g = torch.Generator().manual_seed(3)
+    vid, vflops, vt = {}, 0.0, 0.0
+    for name, N, K in workloads.VIDEO_LINEARS:
+        xv = bf16(workloads.video_activation(srows, K, g))
+        B = weight(bf16((0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)), threads)
+        t = time.perf_counter()
+        f = linear(xv, B, threads)
+        vt += time.perf_counter() - t
+        vflops += f
+    res["video_dit"] = {"all_threads_TFLOPs": round(vflops / vt / 1e12, 6),
+                        "all_threads_s_extrapolated": round(vt * workloads.VIDEO_M / srows, 2),
+                        "sample": f"{srows} rows of each linear (same distribution as the 10240-row activations), "
+                                  f"{vt:.2f} s, extrapolated linearly"}
+    w16 = {}
+    for name, (w, acts) in workloads.w4a16(ms=(1, 16, srows)).items():
+        B = weight(w.numpy(), threads)
+        for m, a in acts.items():
+            A = oracle.bf16_to_f32(bf16(a))
+            t = time.perf_counter()
+            oracle.gemm(A, B, threads=threads)
+            dtm = time.perf_counter() - t
+            w16[f"{name}_M{m}"] = {"s": round(dtm, 4), "TFLOPs": round(2.0 * m * B.shape[0] * B.shape[1] / dtm / 1e12, 6)}
+        w16[f"{name}_M4096_s_extrapolated"] = round(w16[f"{name}_M{srows}"]["s"] * 4096 / srows, 2)
+    res["w4a16"] = w16
+    # quantize + dequantize of a sweep tensor (bf16 4096 x 12288)
+    xs = bf16(workloads.sweep(4096, 12288))
+    t = time.perf_counter()
+    p, sc, S = oracle.quantize(xs, threads=threads)
+    tq = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.dequantize(p, sc, S, threads=threads)
+    td = time.perf_counter() - t
+    n = xs.size
+    res["sweep_4096x12288"] = {"quantize_dynamic_GBps": round(n * 4.5625 / tq / 1e9, 2),
+                               "dequantize_GBps": round(n * 2.5625 / td / 1e9, 2)}
+    res["value"] = round(value, 6)
+    res["unit"] = "TFLOP/s"
+    res["cores"] = threads
+    res["sample"] = (f"the whole PixArt block (all {layers[0]['M']} rows of every linear: tensor scale, quantize, "
+                     f"dequantize, fp64-accumulated GEMM), {dt:.2f} s on {threads} threads of {host['model']}")
+    return res
 
 
 if __name__ == "__main__":

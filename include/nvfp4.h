@@ -53,20 +53,28 @@ typedef enum {
   NVFP4_ERR_MODE = 6,      /* unknown mode */
   NVFP4_ERR_WORKSPACE = 7, /* workspace required but NULL or smaller than the query says */
   NVFP4_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed */
-  NVFP4_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+  NVFP4_ERR_DEVICE = 9,    /* the current device is not a gfx950 GPU */
+  /* Range sentinels (not statuses): they give every enum of this header the full range of int, so
+     any int a caller passes -- including an invalid one, which the calls reject -- is a value of
+     the type on both sides of the C / C++ boundary. */
+  NVFP4_STATUS_MIN_ENUM_ = -0x7fffffff - 1,
+  NVFP4_STATUS_MAX_ENUM_ = 0x7fffffff
 } nvfp4_status_t;
 
-typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_DTYPE_MIN_ENUM_ = -0x7fffffff - 1,
+               NVFP4_DTYPE_MAX_ENUM_ = 0x7fffffff } nvfp4_dtype_t;
 
 /* W4A4: both operands NVFP4 [NVFP4-DiT page, Methodology section 3; vllm-omni RFC, Open
    Question 1].  W4A16: bf16 activations times an NVFP4 weight (weight-only quantization,
    vllm-omni RFC Open Question 1; kandinsky-5 NVFP4 pull request, Summary). */
-typedef enum { NVFP4_W4A4 = 0, NVFP4_W4A16 = 1 } nvfp4_mode_t;
+typedef enum { NVFP4_W4A4 = 0, NVFP4_W4A16 = 1, NVFP4_MODE_MIN_ENUM_ = -0x7fffffff - 1,
+               NVFP4_MODE_MAX_ENUM_ = 0x7fffffff } nvfp4_mode_t;
 
 /* DYNAMIC: the call computes S from the input and writes it.  STATIC: the call reads a
    caller-given S (the pages' static / calibrated scale: NVFP4-DiT page, Highlights, "Static FP4";
    vllm-omni RFC, Open Question 2). */
-typedef enum { NVFP4_SCALE_DYNAMIC = 0, NVFP4_SCALE_STATIC = 1 } nvfp4_scale_mode_t;
+typedef enum { NVFP4_SCALE_DYNAMIC = 0, NVFP4_SCALE_STATIC = 1, NVFP4_SCALE_MIN_ENUM_ = -0x7fffffff - 1,
+               NVFP4_SCALE_MAX_ENUM_ = 0x7fffffff } nvfp4_scale_mode_t;
 
 /* Short English text for a status; never NULL. */
 const char *nvfp4_status_string(nvfp4_status_t status);
@@ -253,7 +261,8 @@ nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t x_dtype, int6
  *                  the same query with lda == K.  A shorter workspace returns NVFP4_ERR_WORKSPACE.
  *   M == 0 or N == 0 is valid and touches nothing.
  * ------------------------------------------------------------------------------------------- */
-typedef enum { NVFP4_ACT_NONE = 0, NVFP4_ACT_GELU_TANH = 1 } nvfp4_act_t;
+typedef enum { NVFP4_ACT_NONE = 0, NVFP4_ACT_GELU_TANH = 1, NVFP4_ACT_MIN_ENUM_ = -0x7fffffff - 1,
+               NVFP4_ACT_MAX_ENUM_ = 0x7fffffff } nvfp4_act_t;
 
 size_t nvfp4_gemm_requant_workspace_bytes(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K);
 size_t nvfp4_gemm_requant_workspace_bytes_ld(nvfp4_mode_t mode, int64_t M, int64_t N, int64_t K, int64_t lda);

@@ -81,6 +81,7 @@ const char *nvfp4_status_string(nvfp4_status_t s) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_HIP: return "HIP runtime error";
     case NVFP4_ERR_DEVICE: return "current device is not gfx950";
+    default: break;
   }
   return "unknown status";
 }
