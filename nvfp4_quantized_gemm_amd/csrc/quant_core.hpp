@@ -94,11 +94,13 @@ __device__ __forceinline__ uint32_t codes_exact(const float *v, float e, float S
 // boundary differs from it by at least 2^-8 relative, far outside the 2^-19 bracket: an
 // ambiguous bracket is an exact tie, whose code is the even one of the two adjacent bracketing
 // codes (ties to even).  That choice is made for all nibbles at once with integer operations.
-template <int N>
+//
+// kFast: the caller has checked qc.fast_ok (the check then leaves the hot loop).
+template <int N, bool kFast = false>
 __device__ __forceinline__ uint32_t encode_values(const float *v, uint32_t byte, const QuantConsts &qc) {
   const float e = e4m3_to_f32(byte);
   const float S = qc.S;
-  if (qc.fast_ok) {
+  if (kFast || qc.fast_ok) {
     const float inv = __builtin_amdgcn_rcpf(e) * qc.invS;
     const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
     uint32_t lo = 0, hi = 0;
@@ -144,10 +146,12 @@ __device__ __forceinline__ uint32_t encode_values(const float *v, uint32_t byte,
 }
 
 // E4M3 byte of the block maximum amax (>= 0) under S: bracketing fast path, exact fallback.
+// kFast: the caller has checked qc.fast_ok.
+template <bool kFast = false>
 __device__ __forceinline__ uint32_t block_byte(float amax, const QuantConsts &qc) {
   if (!(amax > 0.0f)) return 0u;
   const float S = qc.S;
-  if (qc.fast_ok) {
+  if (kFast || qc.fast_ok) {
     const float ra = fminf(amax * qc.rlo, kE4M3Max), rb = fminf(amax * qc.rhi, kE4M3Max);
     const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
     const uint32_t b0 = pk & 0xffu, b1 = (pk >> 8) & 0xffu;

@@ -14,7 +14,8 @@
 // flight (two for inputs small enough for the caches); a large input is read with streaming
 // (non-temporal) loads, its last use.  Dynamic mode runs k_amax first (same mapping,
 // per-workgroup partial maxima, no atomics, deterministic); every quantize workgroup reduces those
-// partials itself and derives S = RN32(amax / 2688).
+// partials itself and derives S = RN32(amax / 2688), or, on a large tensor, one workgroup does that
+// once (k_tensor_scale) and a widened grid encodes.
 //
 // Exactness (all fast paths bracket the exact real quotient and fall back when unsure):
 //  * Block scale.  With c = 1/(6 S) (fp64, once per workgroup), rl = RN32(amax RN32(c (1 - 2^-20)))
@@ -136,17 +137,29 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// Tensor scale S = RN32(amax / 2688) from the amax pass's partial maxima, in one workgroup.
+__global__ __launch_bounds__(256) void k_tensor_scale(const float *__restrict__ partial, int npartial,
+                                                      float *__restrict__ tensor_scale) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *tensor_scale = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / kDynDivisor;
+}
+
 // ---- quantize ------------------------------------------------------------------------------------
 
 // YT < 0: write the NVFP4 tensor (packed codes + scale bytes).  YT = 0 / 1: fake quantization,
 // write dequantize(quantize(x)) as fp32 / bf16 into y [.][ld_y] instead (one pass, same values as
 // the two calls).
 template <int DT, bool DYNAMIC, bool DENSE, int YT, int BLK, bool NT>
-__global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
-                                                  FastDiv bpr, uint8_t *__restrict__ packed,
-                                                  uint8_t *__restrict__ scales, float *__restrict__ tensor_scale,
-                                                  const float *__restrict__ partial, int npartial,
-                                                  void *__restrict__ y, int64_t ld_y) {
+__device__ __forceinline__ void quantize_body(const void *__restrict__ x, int64_t ld, uint64_t nseg, FastDiv bpr,
+                                              uint8_t *__restrict__ packed, uint8_t *__restrict__ scales,
+                                              float *__restrict__ tensor_scale, const float *__restrict__ partial,
+                                              int npartial, void *__restrict__ y, int64_t ld_y) {
   using In = SegIn<DT>;
   constexpr int E = In::kElems;
   using Map = Segments<E, BLK>;  // a block of BLK values spans Map::kLanesPerBlock adjacent lanes
@@ -189,24 +202,79 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   const float S = s_S;
   const QuantConsts qc = make_quant_consts(S, DT == 1);
 
-  // encodes one segment (its E values already unpacked) as segment g
-  auto encode_seg = [&](const float (&v)[E], uint64_t g) {
-    // block maximum over the block's lanes (nseg is a multiple of the lanes per block, so a
-    // block's lanes are all in range or all out of range)
+  // block maximum over the block's lanes (nseg is a multiple of the lanes per block, so a block's
+  // lanes are all in range or all out of range)
+  auto block_amax = [&](const float (&v)[E]) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = group_max<Map::kLanesPerBlock>(amax);
-    if (g >= nseg) return;
-    const uint32_t byte = block_byte(amax, qc);
-    uint32_t codes;
+    return group_max<Map::kLanesPerBlock>(amax);
+  };
+  // scale byte and codes of one segment of a block with maximum amax (kFast: qc.fast_ok holds)
+  auto encode_block = [&](auto fast_tag, const float (&v)[E], float amax, uint32_t &byte) {
+    constexpr bool kFast = decltype(fast_tag)::value;
+    byte = block_byte<kFast>(amax, qc);
+    uint32_t codes = 0;
     if (byte == 0) {  // zero or flushed block: magnitude 0, sign copied
-      codes = 0;
 #pragma unroll
       for (int i = 0; i < E; ++i) codes |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
     } else {
-      codes = encode_values<E>(v, byte, qc);
+      codes = encode_values<E, kFast>(v, byte, qc);
     }
+    return codes;
+  };
+
+  // Dense NVFP4 output: the tiles wholly inside the tensor run with one base address per tile and
+  // constant offsets for the lane's segments, and two register sets take turns holding the next
+  // tile's loads (no copies).  The one partial tile, if any, goes through the general loop below.
+  // This loop runs for S inside the brackets' window (it then carries no per-block test of the
+  // window); an extreme S takes the general loop throughout.
+  if constexpr (DENSE && YT < 0) {
+    const uint64_t nfull = nseg / (64 * U);
+    auto dense_loop = [&](auto fast_tag) {
+      const u32x4 *xs = static_cast<const u32x4 *>(x) + lane;
+      auto fetch_full = [&](uint64_t tt, u32x4 (&r)[U]) {
+        const u32x4 *p = xs + tt * (64 * U);
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = load16<NT>(p + u * 64);
+      };
+      auto run_tile = [&](const u32x4 (&r)[U], uint64_t tt) {
+        const uint64_t g0 = tt * (64 * U) + lane;  // segment of u = 0; u adds 64
+        uint8_t *pk = packed + (E / 2) * g0;
+        uint8_t *sc = scales + (g0 >> Map::kShift);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float v[E];
+          In::unpack(r[u], v);
+          uint32_t byte;
+          const uint32_t codes = encode_block(fast_tag, v, block_amax(v), byte);
+          if (E == 8) *reinterpret_cast<uint32_t *>(pk + u * 64 * 4) = codes;
+          else *reinterpret_cast<uint16_t *>(pk + u * 64 * 2) = (uint16_t)codes;
+          if ((lane & (Map::kLanesPerBlock - 1)) == 0) sc[u * (64 >> Map::kShift)] = (uint8_t)byte;
+        }
+      };
+      u32x4 alt[U];
+      for (;;) {
+        if (t + tstride < nfull) fetch_full(t + tstride, alt);
+        run_tile(nxt, t);
+        t += tstride;
+        if (t >= nfull) break;
+        if (t + tstride < nfull) fetch_full(t + tstride, nxt);
+        run_tile(alt, t);
+        t += tstride;
+        if (t >= nfull) break;
+      }
+      if (t < ntiles) fetch(t, nxt);
+    };
+    if (t < nfull && qc.fast_ok) dense_loop(std::true_type{});
+  }
+
+  // encodes one segment (its E values already unpacked) as segment g
+  auto encode_seg = [&](const float (&v)[E], uint64_t g) {
+    const float amax = block_amax(v);
+    if (g >= nseg) return;
+    uint32_t byte;
+    const uint32_t codes = encode_block(std::false_type{}, v, amax, byte);
     if (YT < 0) {
       if constexpr (kOutNT) {
         if (E == 8) __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(packed + 4 * g));
@@ -238,6 +306,26 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ x, in
   }
 }
 
+// The NVFP4-output kernel is held to 96 VGPRs, five waves per SIMD: on a 805 MB bf16 tensor this
+// moved the static pass from 190 to 175 us.  Fake quantization keeps the compiler's choice (under
+// the same cap it spills inside its loop).
+template <int DT, bool DYNAMIC, bool DENSE, int BLK, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_quantize(
+    const void *__restrict__ x, int64_t ld, uint64_t nseg, FastDiv bpr, uint8_t *__restrict__ packed,
+    uint8_t *__restrict__ scales, float *__restrict__ tensor_scale, const float *__restrict__ partial, int npartial) {
+  quantize_body<DT, DYNAMIC, DENSE, -1, BLK, NT>(x, ld, nseg, bpr, packed, scales, tensor_scale, partial, npartial,
+                                                 nullptr, 0);
+}
+
+template <int DT, bool DYNAMIC, bool DENSE, int YT, int BLK>
+__global__ __launch_bounds__(256) void k_fake_quantize(const void *__restrict__ x, int64_t ld, uint64_t nseg,
+                                                       FastDiv bpr, float *__restrict__ tensor_scale,
+                                                       const float *__restrict__ partial, int npartial,
+                                                       void *__restrict__ y, int64_t ld_y) {
+  quantize_body<DT, DYNAMIC, DENSE, YT, BLK, true>(x, ld, nseg, bpr, nullptr, nullptr, tensor_scale, partial,
+                                                   npartial, y, ld_y);
+}
+
 // ---- launchers -------------------------------------------------------------------------------------
 
 static int grid_for(uint64_t nseg, int cap, int segs) {
@@ -252,21 +340,34 @@ template <int DT, bool DENSE, int YT, int BLK>
 static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr16, FastDiv bpr, uint8_t *packed,
                          uint8_t *scales, float *tensor_scale, bool dynamic, float *partial, void *y, int64_t ld_y,
                          hipStream_t stream) {
-  // the dynamic NVFP4 pass keeps the resident grid (every workgroup also reduces the amax
-  // partials); the others widen it on large tensors
+  // Large tensors widen the encode grid.  A dynamic pass then reduces the amax partials once
+  // (k_tensor_scale, one workgroup) and runs the static kernel, which reads S; on smaller tensors
+  // every encode workgroup of the resident grid reduces the partials itself (one launch fewer).
   auto run = [&](auto nt_tag) {
     constexpr bool NT = decltype(nt_tag)::value;
     constexpr int U = segs_per_lane<NT>();
-    const bool wide = (!dynamic || YT >= 0) && grid_for(nseg, 1 << 30, U) > 4 * kQuantizeMaxGrid;
+    const bool wide = grid_for(nseg, 1 << 30, U) > 4 * kQuantizeMaxGrid;
     const int gq = grid_for(nseg, wide ? kQuantizeWideGrid : kQuantizeMaxGrid, U);
+    const int ga = dynamic ? grid_for(nseg, kAmaxPartials, U) : 0;
     if (dynamic) {
-      const int ga = grid_for(nseg, kAmaxPartials, U);
       k_amax<DT, DENSE, NT><<<ga, 256, 0, stream>>>(x, ld, nseg, bpr16, partial);
-      k_quantize<DT, true, DENSE, YT, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales,
-                                                                       tensor_scale, partial, ga, y, ld_y);
+      if (wide) k_tensor_scale<<<1, 256, 0, stream>>>(partial, ga, tensor_scale);
+    }
+    const bool dyn_kernel = dynamic && !wide;
+    if constexpr (YT < 0) {
+      if (dyn_kernel)
+        k_quantize<DT, true, DENSE, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
+                                                                     partial, ga);
+      else
+        k_quantize<DT, false, DENSE, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales, tensor_scale,
+                                                                      nullptr, 0);
     } else {
-      k_quantize<DT, false, DENSE, YT, BLK, NT><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales,
-                                                                        tensor_scale, nullptr, 0, y, ld_y);
+      if (dyn_kernel)
+        k_fake_quantize<DT, true, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, tensor_scale, partial, ga,
+                                                                          y, ld_y);
+      else
+        k_fake_quantize<DT, false, DENSE, YT, BLK><<<gq, 256, 0, stream>>>(x, ld, nseg, bpr, tensor_scale, nullptr, 0,
+                                                                           y, ld_y);
     }
   };
   if constexpr (YT >= 0) {
