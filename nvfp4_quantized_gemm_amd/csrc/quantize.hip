@@ -137,11 +137,26 @@ __global__ __launch_bounds__(256) void k_amax(const void *__restrict__ x, int64_
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// This thread's share of the maximum of the npartial (<= kAmaxPartials) partial maxima: all of its
+// loads are issued before the first comparison.
+__device__ __forceinline__ float partial_max(const float *__restrict__ partial, int npartial) {
+  static_assert(kAmaxPartials % 256 == 0, "partials per thread");
+  float v[kAmaxPartials / 256];
+#pragma unroll
+  for (int j = 0; j < kAmaxPartials / 256; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    v[j] = i < npartial ? partial[i] : 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kAmaxPartials / 256; ++j) m = fmaxf(m, v[j]);
+  return m;
+}
+
 // Tensor scale S = RN32(amax / 2688) from the amax pass's partial maxima, in one workgroup.
 __global__ __launch_bounds__(256) void k_tensor_scale(const float *__restrict__ partial, int npartial,
                                                       float *__restrict__ tensor_scale) {
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
+  float m = partial_max(partial, npartial);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float red[4];
@@ -182,8 +197,7 @@ __device__ __forceinline__ void quantize_body(const void *__restrict__ x, int64_
 
   __shared__ float s_S;
   if (DYNAMIC) {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
+    float m = partial_max(partial, npartial);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     __shared__ float red[4];
