@@ -24,13 +24,16 @@ inline hipError_t set_dynamic_lds(const void *kern, int bytes, std::atomic<bool>
 }
 
 constexpr int kAmaxPartials = 1024;     // max workgroups of the dynamic amax pass (= partials)
-// Grid caps (grid-stride beyond).  The quantize kernel runs at most 2048 workgroups (its registers
-// allow four or five per CU at once), each prefetching its next tile; passes that write more than
-// they read (static quantization and fake quantization of large tensors) measured faster with
-// 16384.  The dequantize kernel, write-dominated too, runs one workgroup per four tiles up to a
-// large cap.
-constexpr int kQuantizeMaxGrid = 2048;
+// Grid caps (grid-stride beyond).  The quantize kernel runs at most 1280 workgroups, the five per
+// CU that its 96 registers allow at once, each prefetching its next tile (2048, which left a
+// second partial round, was 0.5-0.8 us slower on 37.7 and 63 MB activations); tensors with more
+// than 8192 workgroups' worth of tiles run 16384 (measured faster for every pass there).  The
+// MXFP4 quantize keeps 2048.  The dequantize kernel, write-dominated, runs one workgroup per four
+// tiles up to a large cap.
+constexpr int kQuantizeMaxGrid = 1280;
+constexpr int kQuantizeWideFrom = 8192;
 constexpr int kQuantizeWideGrid = 16384;
+constexpr int kMxQuantizeMaxGrid = 2048;
 constexpr int kDequantizeMaxGrid = 1 << 20;
 
 // blk: values per E4M3 scale byte along K (16, 32 or 64)

@@ -456,7 +456,7 @@ hipError_t launch_mx_quantize(const void *x, int dtype, int64_t M, int64_t K, in
                               uint8_t *scales, hipStream_t stream) {
   const FastDiv bpr = make_fastdiv((uint32_t)(K / kMxBlk));
   const uint64_t nseg = (uint64_t)M * (uint64_t)K / (dtype == 0 ? 4u : 8u);
-  const int grid = mx_grid(nseg, kQuantizeMaxGrid);
+  const int grid = mx_grid(nseg, kMxQuantizeMaxGrid);
   const bool dense = (ld == K);
   if (dtype == 0) {
     if (dense) k_mx_quantize<0, true><<<grid, 256, 0, stream>>>(x, ld, nseg, bpr, packed, scales);

@@ -360,7 +360,7 @@ static void run_quantize(const void *x, int64_t ld, uint64_t nseg, FastDiv bpr16
   auto run = [&](auto nt_tag) {
     constexpr bool NT = decltype(nt_tag)::value;
     constexpr int U = segs_per_lane<NT>();
-    const bool wide = grid_for(nseg, 1 << 30, U) > 4 * kQuantizeMaxGrid;
+    const bool wide = grid_for(nseg, 1 << 30, U) > kQuantizeWideFrom;
     const int gq = grid_for(nseg, wide ? kQuantizeWideGrid : kQuantizeMaxGrid, U);
     const int ga = dynamic ? grid_for(nseg, kAmaxPartials, U) : 0;
     if (dynamic) {
