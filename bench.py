@@ -591,7 +591,7 @@ def block_size_section(layers, side, stream, reps):
 
 
 def other_configs_section(side, stream, reps):
-    """The video-DiT linears (M = 10240 tokens, hidden 3072; Student-t activations with log-normal
+    """The tiny linear (M = 256, K = N = 1152, fp32 activation and output); the video-DiT linears (M = 10240 tokens, hidden 3072; Student-t activations with log-normal
     channel scales, seed 3) as in the step: dynamic activation quantize + W4A4 GEMM with bf16 output
     per linear; and the weight-only GEMM at the matrix-bound row counts M = 256 and 4096 (seed 2
     weights).  Each call is timed as back-to-back launches in one graph, the better of two timings."""
@@ -601,7 +601,29 @@ def other_configs_section(side, stream, reps):
     import workloads
 
     dev = "cuda"
-    res = {"video_dit_w4a4": {}, "w4a16_matrix_bound": {}}
+    res = {"tiny_w4a4": {}, "video_dit_w4a4": {}, "w4a16_matrix_bound": {}}
+    # the tiny linear (X fp32 [256, 1152], W [1152, 1152], seed 0): dynamic quantize of X, W4A4 GEMM
+    # with fp32 output
+    x, w = workloads.tiny()
+    M, K = x.shape
+    N = w.shape[0]
+    xd = x.to(dev)
+    wp, ws, wS = nv.nvfp4_quantize(w.to(dev))
+    bp = nv.nvfp4_prepack_weight(wp, ws)
+    pa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    Sa = torch.empty(1, dtype=torch.float32, device=dev)
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gws = torch.empty(max(1, nv.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K)), dtype=torch.uint8, device=dev)
+    q_us = min(time_graph([lambda: nv.nvfp4_quantize(xd, Sa, static=False, packed=pa, scales=sa, workspace=qws)]
+                          * reps, side, stream) for _ in range(2))
+    g_us = min(time_graph([lambda: nv.nvfp4_gemm(nv.W4A4, pa, sa, Sa, bp, wS, N, K, torch.float32, out=y,
+                                                 workspace=gws)] * reps, side, stream) for _ in range(2))
+    tf = 2.0 * M * N * K / (g_us * 1e-6) / 1e12
+    res["tiny_w4a4"] = {"M": M, "N": N, "K": K, "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2),
+                        "gemm_TFLOPs": round(tf, 1), "gemm_frac": round(tf / PEAK_FP16_TFLOPS, 4)}
+    del xd, wp, ws, bp, pa, sa, y, gws, qws
     step_us, flops_step = 0.0, 0.0
     for name, x, w in workloads.video():
         M, K = x.shape
