@@ -22,7 +22,7 @@ import torch
 import nvfp4_quantized_gemm_amd as nv
 import oracle
 import workloads
-from test_gpu_parity import DEV, Guarded, assert_quantize_exact, check_gemm, np_bf16, np_x, say
+from test_gpu_parity import DEV, Guarded, assert_quantize_exact, check_gemm, np_bf16, np_x, run_fake, say
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,14 @@ def test_gemm_video_sampled_with_edges():
         assert Sa == SA and Sb == SB
         Y, R = oracle.gemm(A, B)
         check_gemm(Yg[np.ix_(rows, cols)], Y, R, True, f"video {name} edges")
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_fake_quantize_large_tensor(static):
+    """Fake quantization (bf16 out) of the 32768 x 3072 sweep tensor: large enough for the widened
+    grid, where a dynamic pass reduces the amax partials once in its own kernel."""
+    x = workloads.sweep(32768, 3072, static=static)
+    run_fake(x, workloads.SWEEP_STATIC_S if static else None, torch.bfloat16, label="sweep 32768x3072")
 
 
 # ---- row-strided W4A4 activations ---------------------------------------------------------------------
