@@ -779,11 +779,29 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   // Fewer big tiles than CUs.  128x128 tiles run two workgroups per CU: when their grid fits one
   // round (<= one per CU, or close to two per CU everywhere, or K short enough that the uneven
   // share costs little) they beat splitting K over 256x256 tiles, whose partials cost HBM traffic
-  // and a reduction; a small grid with long K splits K two ways too (each split >= 16 chunks).
+  // and a reduction.
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (t128 <= cus) {
+    // At most one 128x128 tile per CU: splitting K over the idle CUs pays when the chunks saved
+    // outweigh the fp32 partials and the reduction launch.  Cost model fit to a sweep (M 256 ..
+    // 1024, N 1152 / 3072, K 1152 .. 4608, splits 1 .. 6; it picks the fastest split or one
+    // within 1 us on all 15 shapes): chunks per split x 0.9 us (x 1.7 where two workgroups share
+    // a CU), plus 2 us + splits x M N x 8 B at 2.9 TB/s for a split (256 x 1152 x 1152: 12.1 ->
+    // 10.8 us; 256 x 3072 x 4608: 37.3 -> 22.9 us).
     pl.variant = GemmVariant::W4A4_128x128;
-    pl.splits = (2 * t128 <= cus && Kc >= 32 && N % 4 == 0) ? 2 : 1;
+    pl.splits = 1;
+    if (N % 4 == 0) {
+      double best = 0.9 * (double)Kc;
+      for (int sp = 2; sp <= 6; ++sp) {
+        if (Kc / sp < 2 || t128 * sp > 2 * cus) continue;
+        const double t = 0.9 * (double)((Kc + sp - 1) / sp) * (t128 * sp > cus ? 1.7 : 1.0) + 2.0 +
+                         (double)sp * (double)M * (double)N * 8.0 / 2.9e6;
+        if (t < best) {
+          best = t;
+          pl.splits = sp;
+        }
+      }
+    }
     return pl;
   }
   if (t128 <= 2 * cus && (t128 % cus == 0 || t128 % cus >= (3 * cus) / 4 || Kc <= 12)) {

@@ -191,15 +191,17 @@ def test_workspace_queries_follow_the_activation_pitch(L):
     assert rq(L, M=M, N=N, K=K, lda=400, ws=P, wsb=M * N * 4 - 1) == S.ERR_WORKSPACE
     # the bf16 / fp32 output of the generic kernel needs none
     assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == 0
-    # a split-K plan: two fp32 partials with lda = K or K + 128, none for the generic kernel
+    # a split-K plan (16 tiles, 32 chunks: several fp32 partials) with lda = K or K + 128, none for
+    # the generic kernel
     M, N, K = 512, 512, 4096
+    need = L.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K)
+    assert need >= 2 * M * N * 4 and need % (M * N * 4) == 0
     for ld in (K, K + 128):
-        assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == 2 * M * N * 4
-        assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == 2 * M * N * 4
+        assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == need
+        assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, ld) == need
     assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == 0
     assert L.nvfp4_gemm_requant_workspace_bytes_ld(nv.W4A4, M, N, K, K + 16) == M * N * 4
-    assert L.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K) == 2 * M * N * 4
-    assert g(L, M=M, N=N, K=K, lda=K + 128, ldc=N, ws=P, wsb=2 * M * N * 4 - 16) == S.ERR_WORKSPACE
+    assert g(L, M=M, N=N, K=K, lda=K + 128, ldc=N, ws=P, wsb=need - 16) == S.ERR_WORKSPACE
     # W4A16 rows <= 64 stream unless 32 rows of the pitch pass 2 GiB; the tiled plan then decides
     lda = 1 << 26
     assert L.nvfp4_gemm_workspace_bytes_ld(nv.W4A16, 16, 3072, 12288, 12288) == \

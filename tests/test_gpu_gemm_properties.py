@@ -46,7 +46,7 @@ def gemm_case(draw):
 @example(("w4a4", 4096, 1152, 4608, torch.bfloat16, 11))    # 256x256 tiles, three-way K split
 @example(("w4a4", 4096, 4608, 1152, torch.bfloat16, 12))    # one round of 256 tiles + 128 tiles
 @example(("w4a4_b32", 4100, 3000, 1024, torch.float32, 13))  # two rounds of 256 tiles
-@example(("w4a4", 512, 512, 4096, torch.float32, 14))       # 128x128 tiles, two-way K split
+@example(("w4a4", 512, 512, 4096, torch.float32, 14))       # 128x128 tiles, K split
 @example(("w4a16", 1024, 3072, 3072, torch.bfloat16, 15))   # 256x256 W4A16 tiles
 @example(("w4a16", 300, 12288, 3072, torch.float32, 16))    # 128x256 W4A16 tiles
 @example(("w4a16", 16, 512, 4096, torch.float32, 17))       # streaming kernel, K split

@@ -57,7 +57,7 @@ def test_graph_replay_all_paths():
     NVFP4-output GEMM, and MXFP4 quantize + GEMM; each replay equals the eager run bit for bit."""
     dev = "cuda"
     g = torch.Generator().manual_seed(7)
-    M, N, K = 512, 512, 4096           # 128x128 tiles with a two-way K split
+    M, N, K = 512, 512, 4096           # 128x128 tiles with a K split
     x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev)
     w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16).to(dev)
     x16 = torch.randn(16, K, generator=g).to(torch.bfloat16).to(dev)

@@ -320,7 +320,7 @@ def test_gemm_w4a4_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (512, 512, 4096),     # 16 tiles of 128 x 128, K split two ways
+    (512, 512, 4096),     # 16 tiles of 128 x 128, K split
     (4096, 1024, 4096),   # 256 tiles of 128 x 128, one per CU
     (2048, 4096, 1024),   # 512 tiles of 128 x 128, two per CU
     (3072, 1408, 2048),   # 264 small tiles, uneven: 256 x 256 tiles with K split two ways
