@@ -333,6 +333,22 @@ def test_gemm_w4a4_planner_paths(M, N, K):
     run_w4a4(x, w, torch.bfloat16, sample=(64, 64))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (256, 1152, 2304),    # 18 tiles of 128 x 128, 18 chunks: split six ways, three chunks each
+    (256, 3072, 4608),    # 48 tiles, 36 chunks: split four ways
+    (512, 1152, 4608),    # 36 tiles: split four ways (9 chunks each)
+    (1024, 1152, 4608),   # 72 tiles: split three ways
+    (300, 1000, 2304),    # ragged M and N with a K split (18 tiles of 128 x 128)
+])
+def test_gemm_w4a4_small_m_split_plans(M, N, K):
+    """Every output of the W4A4 GEMM at small-M shapes whose 128 x 128 plan splits K over the idle
+    CUs (the splits differ in their chunk counts when K does not divide evenly)."""
+    g = torch.Generator().manual_seed(M + 2 * N + K)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    run_w4a4(x, w, torch.float32)
+
+
 def test_gemm_w4a4_pixart_full_size_sampled():
     for name, x, w in workloads.pixart():
         run_w4a4(x, w, torch.bfloat16, sample=(96, 96))
