@@ -170,6 +170,40 @@ def main():
     torch.cuda.synchronize()
     ms_step_1 = t0.elapsed_time(t1) / args.steps
 
+    # ---- the same step with calibrated (static) activation scales: each S taken from the dynamic
+    # run, so one encode pass per quantize instead of amax + encode; the outputs must not change ---
+    for L in layers:
+        L["S_cal"] = L["S"].clone()
+
+    def step_static():
+        for L in layers:
+            nv.nvfp4_quantize(L["x"], L["S_cal"], static=True, packed=L["packed"], scales=L["scales"])
+            nv.nvfp4_gemm(nv.W4A4, L["packed"], L["scales"], L["S_cal"], L["bp"], L["wS"], L["N"], L["K"],
+                          torch.bfloat16, out=L["y"], workspace=L["gws"])
+
+    side.wait_stream(torch.cuda.current_stream())
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gs, stream=side):
+            for _ in range(G):
+                step_static()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for L in layers:
+        L["y"].zero_()
+    gs.replay()
+    torch.cuda.synchronize()
+    for L, ref in zip(layers, eager):
+        if not torch.equal(L["y"], ref):
+            raise RuntimeError(f"static-scale step differs from the dynamic result for {L['name']}")
+    t0.record(stream)
+    for _ in range(args.steps // G):
+        gs.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_static = t0.elapsed_time(t1) / args.steps
+    del gs
+
     # ---- per-kernel durations: graphs of back-to-back launches of one kernel -----------------------
     def kernel_us(fn, L):
         g = torch.cuda.CUDAGraph()
@@ -234,6 +268,11 @@ def main():
                    "linears": {L["name"]: [L["K"], L["N"]] for L in layers}, "parallelism": "none (1 GPU)",
                    "timing": f"HIP-graph replay, {G} steps per graph"},
         "ms_per_step_one_step_per_graph": round(ms_step_1, 4),
+        "static_activation_scales": {
+            "ms_per_step": round(ms_step_static, 4),
+            "TFLOPs": round(flops_step / (ms_step_static * 1e-3) / 1e12, 2),
+            "note": "the same step with each activation's S calibrated (taken from the dynamic run): one "
+                    "encode pass per quantize; outputs identical to the dynamic step"},
         "roofline": roofline,
         "quantize": {"achieved_GBps": round(q_total_bytes / (q_total_us * 1e-6) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
                      "frac": round(q_total_bytes / (q_total_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
