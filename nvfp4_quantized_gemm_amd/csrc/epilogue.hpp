@@ -61,11 +61,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
     const bool interior = vec && (row0 + i * 32 + 31 < M) && (col0 + CW <= N);
     if (interior) {
       OutT *pc = C + (int64_t)(row0 + i * 32 + rr) * ldc + (col0 + cq);
+      // every read of the slab first (one LDS latency), then the stores
+      u32x4 vals[32 / kRowsPerRead];
 #pragma unroll
-      for (int t = 0; t < 32 / kRowsPerRead; ++t) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + (t * kRowsPerRead + rr) * kPitch + cq * ES);
-        store16<NT>(pc + (int64_t)(t * kRowsPerRead) * ldc, v);
-      }
+      for (int t = 0; t < 32 / kRowsPerRead; ++t)
+        vals[t] = *reinterpret_cast<const u32x4 *>(lds + (t * kRowsPerRead + rr) * kPitch + cq * ES);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 32 / kRowsPerRead; ++t) store16<NT>(pc + (int64_t)(t * kRowsPerRead) * ldc, vals[t]);
       wave_lds_sync();  // the next slab overwrites this region
       continue;
     }
