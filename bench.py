@@ -459,10 +459,23 @@ def hbm_kernels(side, stream):
     res[f"quantize_dynamic_bf16_{M}x{K}_generic_S"]["S"] = float(S.item())
     us = time_graph([lambda: nv.nvfp4_quantize(x, S, static=True, packed=packed, scales=scales)] * reps, side, stream)
     res[f"quantize_static_bf16_{M}x{K}_generic_S"] = entry(us, n * (2 + 0.5625))
+    # measured floors beside 8 TB/s: a device copy of the same bf16 tensor (read + write)
+    us = time_graph([lambda: y.copy_(x)] * reps, side, stream)
+    copy_big = entry(us, n * 4)
+    res[f"copy_bf16_{M}x{K}"] = copy_big
     del x, packed, scales, y
     torch.cuda.empty_cache()
 
     copies = 32
+    # the weight-only calls' floor: a copy of one weight's 21 MB as a dependent launch, rotating over
+    # 32 source buffers like the GEMM calls below
+    wb = 21 << 20
+    srcs = [torch.empty(wb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    dst = torch.empty(wb, dtype=torch.uint8, device=dev)
+    us = time_graph([(lambda s_=s_: dst.copy_(s_)) for s_ in srcs], side, stream)
+    copy_small = entry(us, 2 * wb)
+    res["copy_21MiB_dependent_launch"] = copy_small
+    del srcs, dst
     for name, (w, acts) in workloads.w4a16(ms=(1, 16)).items():
         N, Kw = w.shape
         wp, ws, wS = nv.nvfp4_quantize(w.to(dev))
@@ -479,9 +492,14 @@ def hbm_kernels(side, stream):
             us = time_graph(fns, side, stream)
             e = entry(us, 0.5625 * N * Kw + 2 * m * Kw + 2 * m * N)
             e["TFLOPs"] = round(2.0 * m * N * Kw / (us * 1e-6) / 1e12, 2)
+            e["time_vs_copy_21MiB"] = round(us / copy_small["us"], 3)  # < 1: faster than the copy
             res[f"w4a16_{name}_M{m}_N{N}_K{Kw}"] = e
         del bps
         torch.cuda.empty_cache()
+    # the bandwidth calls of the big tensor against the measured copy rate
+    for k, v in res.items():
+        if k.endswith(f"{M}x{K}") or k.endswith("_generic_S"):
+            v["frac_of_copy"] = round(v["GBps"] / copy_big["GBps"], 4)
     return res
 
 
