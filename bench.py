@@ -6,15 +6,16 @@ activation (amax pass + quantize pass) followed by the W4A4 GEMM with bf16 outpu
 quantized and prepacked once before timing (offline, as a deployed model ships them).  Inputs are
 seeded synthetic tensors resident in device memory before the timed region.
 
-The step's 13 kernel launches (amax, encode and GEMM per linear, plus fc2's split-K reduction)
-are captured in a HIP graph, 10 steps per graph (the largest divisor of K up to 10), and the graph
-is replayed, so host launch overhead is not part of the measurement and each replay's own launch
-latency is paid once per 10 steps, as in a graph of a whole forward pass; the same K steps with
-one step per graph are reported beside the value.  Every replay is checked bit-for-bit against an
-eager run first.  Prints one JSON line: `value` is the block's GEMM work (sum of 2 M N K) divided by the
-measured step time (quantization included).  `roofline` describes the dominant GEMM launch, whose
-average duration is measured with HIP events around graph replays of back-to-back launches of that
-kernel on the stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
+The step's 12 kernel launches (amax, encode and GEMM per linear) are captured in a HIP graph,
+10 steps per graph (the largest divisor of K up to 10), and the graph is replayed, so host launch
+overhead is not part of the measurement and each replay's own launch latency is paid once per 10
+steps, as in a graph of a whole forward pass; the same K steps with one step per graph are
+reported beside the value.  Every replay is checked bit-for-bit against an eager run first.
+
+Prints one JSON line: `value` is the block's GEMM work (sum of 2 M N K) divided by the measured
+step time (quantization included).  `roofline` describes the dominant GEMM launch, whose average
+duration is measured with HIP events around graph replays of back-to-back launches of that kernel
+on the stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
 """
 import argparse
 import json
@@ -314,11 +315,11 @@ KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp", "epilogue.hpp", "quant
 
 
 def gemm_kernels(nv, d):
-    """The kernels one call launches at this shape (the split-K plan needs a workspace)."""
+    """The kernels one call launches at this shape (a split-K plan needs a workspace)."""
     ws = nv.nvfp4_gemm_workspace_bytes(nv.W4A4, d["M"], d["N"], d["K"])
     if ws:
-        return f"k_gemm_tiled 256x256 split-K x{ws // (4 * d['M'] * d['N'])} + k_splitk_reduce"
-    return "k_gemm_tiled"
+        return f"k_gemm_tiled split-K x{ws // (4 * d['M'] * d['N'])} + k_splitk_reduce"
+    return "k_gemm_tiled, one launch"
 
 
 def kernel_source_hash():

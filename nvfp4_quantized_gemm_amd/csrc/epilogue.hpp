@@ -12,10 +12,22 @@ namespace nvfp4 {
 // wave-private, padded, row-major LDS region (one 8- or 16-byte write per column group) and read
 // back row-contiguously, so every global store instruction covers whole rows of the sub-tile with
 // 16-byte lane stores.  `vec` says the rows of C are 16-byte aligned; a lane whose 16 bytes lie
-// inside C stores them at once, lanes at the ragged edge store element by element.
+// inside C stores them at once, lanes at the ragged edge store element by element.  A sub-tile
+// width that is not a power of two (96 columns) is read back as two pieces (64 + 32 columns), each
+// with a whole number of rows per 64-lane read.
 template <int CW, int ES>
 struct EpiPitch {
   static constexpr int kPitch = CW * ES + 16;  // row pitch in bytes (16-B pad against bank conflicts)
+};
+
+// The first read-back piece of a CW-column slab: the largest power of two <= CW (at most 128);
+// the rest (CW minus that) must itself be 0 or a power of two.
+template <int CW>
+struct EpiPieces {
+  static constexpr int kFirst = CW >= 128 ? 128 : (CW >= 64 ? 64 : 32);
+  static constexpr int kRest = CW - kFirst;
+  static_assert(CW % 32 == 0 && CW <= 256, "epilogue width");
+  static_assert(kRest == 0 || kRest == 32 || kRest == 64 || kRest == 128, "epilogue pieces");
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -24,18 +36,64 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Store rows 0..31 of columns [OFF, OFF + PW) of a staged slab (row-major, pitch kPitch bytes) to C
+// at (row_base, col_base + OFF).
+template <int PW, int OFF, int kPitch, typename OutT, bool NT>
+__device__ __forceinline__ void store_slab_piece(const uint8_t *lds, OutT *__restrict__ C, int64_t ldc, int M, int N,
+                                                 int row_base, int col_base, bool vec, int lane) {
+  constexpr int ES = (int)sizeof(OutT);
+  constexpr int kLanesPerRow = PW * ES / 16;
+  constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  constexpr int kEl = 16 / ES;  // elements per 16-byte lane access
+  static_assert(kLanesPerRow <= 64 && 64 % kLanesPerRow == 0 && 32 % kRowsPerRead == 0, "epilogue piece");
+  const int rr = lane / kLanesPerRow, cq = OFF + (lane % kLanesPerRow) * kEl;
+  // A piece wholly inside C (the common case) stores without per-lane bounds checks; the test is
+  // wave-uniform, so interior tiles never execute the ragged-edge code below.
+  const bool interior = vec && (row_base + 31 < M) && (col_base + OFF + PW <= N);
+  if (interior) {
+    OutT *pc = C + (int64_t)(row_base + rr) * ldc + (col_base + cq);
+    // every read of the piece first (one LDS latency), then the stores
+    u32x4 vals[32 / kRowsPerRead];
+#pragma unroll
+    for (int t = 0; t < 32 / kRowsPerRead; ++t)
+      vals[t] = *reinterpret_cast<const u32x4 *>(lds + (t * kRowsPerRead + rr) * kPitch + cq * ES);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 32 / kRowsPerRead; ++t) store16<NT>(pc + (int64_t)(t * kRowsPerRead) * ldc, vals[t]);
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < 32 / kRowsPerRead; ++t) {
+    const int r = t * kRowsPerRead + rr;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r * kPitch + cq * ES);
+    const int row = row_base + r, col = col_base + cq;
+    OutT *pc = C + (int64_t)row * ldc + col;
+    if (vec && row < M && col + kEl <= N) {
+      store16<NT>(pc, v);
+    } else if (row < M && col < N) {
+      // ragged edge: element by element (elements taken out of the registers by shifts, so the
+      // staged vector never goes through memory)
+#pragma unroll
+      for (int q = 0; q < kEl; ++q) {
+        if (col + q < N) {
+          const uint32_t word = v[(q * ES) / 4];
+          if (ES == 4) reinterpret_cast<uint32_t *>(pc)[q] = word;
+          else reinterpret_cast<uint16_t *>(pc)[q] = (uint16_t)(word >> (16 * (q & 1)));
+        }
+      }
+    }
+  }
+}
+
 template <int CW, int TM, int TN, typename OutT, bool NT = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float scale, OutT *__restrict__ C,
                                            int64_t ldc, int M, int N, int row0, int col0, bool vec,
                                            uint8_t *lds, int lane) {
   constexpr int ES = (int)sizeof(OutT);
   constexpr int kPitch = EpiPitch<CW, ES>::kPitch;
-  constexpr int kLanesPerRow = CW * ES / 16;
-  constexpr int kRowsPerRead = 64 / kLanesPerRow;
-  constexpr int kEl = 16 / ES;  // elements per 16-byte lane access
-  static_assert(CW == 32 * TN && kLanesPerRow <= 64 && 64 % kLanesPerRow == 0, "epilogue shape");
+  using Pieces = EpiPieces<CW>;
+  static_assert(CW == 32 * TN, "epilogue shape");
   const int lr = lane & 31, lh = lane >> 5;
-  const int rr = lane / kLanesPerRow, cq = (lane % kLanesPerRow) * kEl;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -56,43 +114,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], float sc
       }
     }
     wave_lds_sync();
-    // A slab wholly inside C (the common case) stores without per-lane bounds checks; the test is
-    // wave-uniform, so interior tiles never execute the ragged-edge code below.
-    const bool interior = vec && (row0 + i * 32 + 31 < M) && (col0 + CW <= N);
-    if (interior) {
-      OutT *pc = C + (int64_t)(row0 + i * 32 + rr) * ldc + (col0 + cq);
-      // every read of the slab first (one LDS latency), then the stores
-      u32x4 vals[32 / kRowsPerRead];
-#pragma unroll
-      for (int t = 0; t < 32 / kRowsPerRead; ++t)
-        vals[t] = *reinterpret_cast<const u32x4 *>(lds + (t * kRowsPerRead + rr) * kPitch + cq * ES);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 32 / kRowsPerRead; ++t) store16<NT>(pc + (int64_t)(t * kRowsPerRead) * ldc, vals[t]);
-      wave_lds_sync();  // the next slab overwrites this region
-      continue;
-    }
-#pragma unroll
-    for (int t = 0; t < 32 / kRowsPerRead; ++t) {
-      const int r = t * kRowsPerRead + rr;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r * kPitch + cq * ES);
-      const int row = row0 + i * 32 + r, col = col0 + cq;
-      OutT *pc = C + (int64_t)row * ldc + col;
-      if (vec && row < M && col + kEl <= N) {
-        store16<NT>(pc, v);
-      } else if (row < M && col < N) {
-        // ragged edge: element by element (elements taken out of the registers by shifts, so the
-        // staged vector never goes through memory)
-#pragma unroll
-        for (int q = 0; q < kEl; ++q) {
-          if (col + q < N) {
-            const uint32_t word = v[(q * ES) / 4];
-            if (ES == 4) reinterpret_cast<uint32_t *>(pc)[q] = word;
-            else reinterpret_cast<uint16_t *>(pc)[q] = (uint16_t)(word >> (16 * (q & 1)));
-          }
-        }
-      }
-    }
+    store_slab_piece<Pieces::kFirst, 0, kPitch, OutT, NT>(lds, C, ldc, M, N, row0 + i * 32, col0, vec, lane);
+    if constexpr (Pieces::kRest > 0)
+      store_slab_piece<Pieces::kRest, Pieces::kFirst, kPitch, OutT, NT>(lds, C, ldc, M, N, row0 + i * 32, col0, vec,
+                                                                        lane);
     wave_lds_sync();  // the next slab overwrites this region
   }
 }
@@ -175,19 +200,44 @@ __device__ __forceinline__ void requant16(float (&v)[16], int64_t row, int64_t c
   }
 }
 
+// Requantize rows 0..31 of columns [OFF, OFF + PW) of a staged fp32 slab: each lane reads back one
+// whole 16-column block of a row.
+template <int PW, int OFF, int kPitch>
+__device__ __forceinline__ void requant_slab_piece(const uint8_t *lds, const QuantOut &qo, const QuantConsts &qc,
+                                                   int M, int N, int row_base, int col_base, int lane) {
+  constexpr int kLanesPerRow = PW / 16;
+  constexpr int kRowsPerRead = 64 / kLanesPerRow;
+  static_assert(64 % kLanesPerRow == 0 && 32 % kRowsPerRead == 0, "epilogue piece");
+  const int rr = lane / kLanesPerRow, cb = OFF + (lane % kLanesPerRow) * 16;
+  // not unrolled: a short slab body lets the slab loop unroll, so the accumulators are only ever
+  // indexed at compile time (no copy in scratch memory)
+#pragma unroll 1
+  for (int t = 0; t < 32 / kRowsPerRead; ++t) {
+    const int r = t * kRowsPerRead + rr;
+    float v[16];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 q = *reinterpret_cast<const f32x4 *>(lds + r * kPitch + (cb + 4 * h) * 4);
+      v[4 * h] = q.x;
+      v[4 * h + 1] = q.y;
+      v[4 * h + 2] = q.z;
+      v[4 * h + 3] = q.w;
+    }
+    const int row = row_base + r, col = col_base + cb;
+    requant16(v, row, col, row < M && col < N, N, qo, qc);
+  }
+}
+
 // store_tile for NVFP4 output: the wave's sub-tile goes through the same padded row-major fp32
-// staging as store_tile; each lane then reads back one whole 16-column block of a row and
-// requantizes it.
+// staging as store_tile, then is requantized block by block.
 template <int CW, int TM, int TN>
 __device__ __forceinline__ void store_tile_nvfp4(const f32x16 (&acc)[TM][TN], float scale, const QuantOut &qo,
                                                  int M, int N, int row0, int col0, uint8_t *lds, int lane) {
   constexpr int kPitch = EpiPitch<CW, 4>::kPitch;
-  constexpr int kLanesPerRow = CW / 16;
-  constexpr int kRowsPerRead = 64 / kLanesPerRow;
-  static_assert(CW == 32 * TN && 64 % kLanesPerRow == 0 && 32 % kRowsPerRead == 0, "epilogue shape");
+  using Pieces = EpiPieces<CW>;
+  static_assert(CW == 32 * TN, "epilogue shape");
   const QuantConsts qc = make_quant_consts(*qo.out_ts, false);
   const int lr = lane & 31, lh = lane >> 5;
-  const int rr = lane / kLanesPerRow, cb = (lane % kLanesPerRow) * 16;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -200,23 +250,9 @@ __device__ __forceinline__ void store_tile_nvfp4(const f32x16 (&acc)[TM][TN], fl
       }
     }
     wave_lds_sync();
-    // not unrolled: a short slab body lets the slab loop unroll, so the accumulators are only ever
-    // indexed at compile time (no copy in scratch memory)
-#pragma unroll 1
-    for (int t = 0; t < 32 / kRowsPerRead; ++t) {
-      const int r = t * kRowsPerRead + rr;
-      float v[16];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const f32x4 q = *reinterpret_cast<const f32x4 *>(lds + r * kPitch + (cb + 4 * h) * 4);
-        v[4 * h] = q.x;
-        v[4 * h + 1] = q.y;
-        v[4 * h + 2] = q.z;
-        v[4 * h + 3] = q.w;
-      }
-      const int row = row0 + i * 32 + r, col = col0 + cb;
-      requant16(v, row, col, row < M && col < N, N, qo, qc);
-    }
+    requant_slab_piece<Pieces::kFirst, 0, kPitch>(lds, qo, qc, M, N, row0 + i * 32, col0, lane);
+    if constexpr (Pieces::kRest > 0)
+      requant_slab_piece<Pieces::kRest, Pieces::kFirst, kPitch>(lds, qo, qc, M, N, row0 + i * 32, col0, lane);
     wave_lds_sync();  // the next slab overwrites this region
   }
 }

@@ -10,10 +10,11 @@
 // (E8M0) scale per 32 k, which cannot represent an E4M3 scale per 16 k, and q * e is not exact in
 // FP8; so the exact route is fp16 (W4A4) / bf16 (W4A16, where A is bf16) MFMA.
 //
-// Kernel structure (k_gemm_tiled): a 256-thread workgroup (4 waves) owns a BM x BN tile and walks
-// K in chunks of 128.  Per chunk it stages, through registers, A codes + A scale bytes (or bf16 A)
-// and one prepacked B unit per 32 columns into an LDS buffer (double-buffered: one barrier per
-// chunk).  Each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  For MFMA step s
+// Kernel structure (k_gemm_tiled): a 256-thread workgroup (4 waves) owns a BM x BN tile (W4A4:
+// 256 x 256, 128 x 128 or 128 x 192; W4A16: 128 x 256 or 256 x 256) and walks K in chunks of 128.
+// Per chunk, LDS-DMA loads stage A codes + A scale bytes (or bf16 A) and one prepacked B unit per
+// 32 columns into a three-stage LDS ring, two chunks ahead of the MFMAs (one barrier per chunk).
+// Each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  For MFMA step s
 // (16 k) lane l = r + 32 h takes k in [64 h + 8 s, +8): that is dword s of the lane's 32-byte code
 // run, so A and B codes are read with 16-byte LDS loads and the k permutation is the same on both
 // sides.  Dequantization in registers: v_cvt_scalef32_pk_{f16,f32}_fp4 with scale 1 gives exact q;
@@ -42,7 +43,11 @@ struct TileCfg {
   static constexpr int kALds = (MODE == 0) ? BM * 64 : (kHalf ? BM * 128 : BM * 256);  // codes or bf16
   static constexpr int kASLds = (MODE == 0) ? BM * 8 : 0;
   static constexpr int kBLds = kHalf ? BN * 32 : BN * 64;
-  static constexpr int kBSLds = BN * 8;
+  // B scale blocks (256 B per 32-column unit) come one per wave per DMA round, so their count is
+  // rounded up to a multiple of the 4 waves: a 192-column tile also fetches the next two units
+  // (clamped to the matrix), whose bytes are never read
+  static constexpr int kBSUnits = (BN / 32 + 3) / 4 * 4;
+  static constexpr int kBSLds = kBSUnits * 256;
   static constexpr int kStage = kALds + kASLds + kBLds + kBSLds;
 };
 
@@ -98,9 +103,10 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // the blocks under its 64 k of a chunk: 4, 2 or 1 bytes, fetched as the aligned dword holding them
 // and shifted into place when read.
 template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK>
-// 128 x 128 tiles need few registers (64 accumulators per wave): two workgroups per CU, so a grid
-// a little larger than the CU count runs in one round; larger tiles one wave per SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <= 128 * 128) ? 2 : 1, (BM * BN <= 128 * 128) ? 2 : 1))) void k_gemm_tiled(
+// 128 x 128 and 128 x 192 tiles need few registers (64 / 96 accumulators per wave): two workgroups
+// per CU, so a grid a little larger than the CU count runs in one round; larger tiles one wave per
+// SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <= 128 * 192) ? 2 : 1, (BM * BN <= 128 * 192) ? 2 : 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
     void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int m_off, int n_off, int splits,
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <=
   constexpr bool HALF = Cfg::kHalf;
   constexpr int NA = (MODE == 0) ? (BM / 32) * 2 : (BM / 32) * (HALF ? 4 : 8);  // 1-KB A blocks per stage
   constexpr int NAS = (MODE == 0) ? BM / 32 : 0;                                 // 256-B A scale blocks
-  constexpr int NB = (BN / 32) * (HALF ? 1 : 2), NBS = BN / 32;
+  constexpr int NB = (BN / 32) * (HALF ? 1 : 2), NBS = Cfg::kBSUnits;
   static_assert(NA % 4 == 0 && NB % 4 == 0 && NBS % 4 == 0 && NAS % 4 == 0, "block counts");
   static_assert(4 * 32 * EpiPitch<BN / WN, 4>::kPitch <= 3 * Cfg::kStage, "epilogue staging fits the LDS ring");
   constexpr int kAStep = (MODE == 0) ? 64 : 256;  // A bytes per row per chunk
@@ -714,8 +720,9 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Plan: which tile kernel(s), how many K splits, and an optional split of N into a region of
-// 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
+// Plan: which tile kernel(s) (W4A4: 256x256, 128x192 or 128x128; W4A16: 128x256, 256x256 or the
+// skinny kernel), how many K splits, and an optional split of N into a region of 256x256 tiles
+// (exactly one round on the chip) plus a remainder of 128x128 tiles.
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   GemmPlan pl;
   const int64_t arow_bytes = (mode == 0) ? lda / 2 : lda * 2;
@@ -766,6 +773,22 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
     return pl;
   }
   const int64_t tmb = (M + 255) / 256, tnb = (N + 255) / 256, tb = tmb * tnb;
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  // 128 x 192 tiles (two workgroups per CU at most): where 128 x 128 tiles put two workgroups on
+  // some CUs and 128 x 192 tiles need fewer workgroups per CU, and 256 x 256 tiles would either fit
+  // one round (then only when 128 x 192 takes at most two per CU) or need a second round.  A lone
+  // 128 x 192 workgroup runs a chunk in ~1.34 us, two on a CU in ~2.5 us, against 0.9 / 1.53 us
+  // for 128 x 128 and 2.9 us for 256 x 256 (one per CU), and there is no K split: PixArt proj
+  // 4096 x 1152 x 1152 22.0 -> 18.3 us, fc2 4096 x 1152 x 4608 62.5 -> 54.5 us (no fp32 partials),
+  // fc1 4096 x 4608 x 1152 57.7 -> 46.8 us (one launch instead of 256 x 256 plus 128 x 128 tiles);
+  // qkv 4096 x 3456 x 1152 stays on 256 x 256 (39.6 against 42.5 us) -- one machine, 40 shapes
+  // M 300..8192, N 768..4608, K 1152 / 4608, all consistent with this rule.
+  const int64_t t192 = ((M + 127) / 128) * ((N + 191) / 192);
+  const int64_t w128 = (t128 + cus - 1) / cus, w192 = (t192 + cus - 1) / cus;
+  if (t128 > cus && w192 < w128 && (w192 <= 2 || (tb > cus && w192 <= 3))) {
+    pl.variant = GemmVariant::W4A4_128x192;
+    return pl;
+  }
   pl.variant = GemmVariant::W4A4_256x256;
   if (tb >= cus) {
     // more than one round: cover whole big-tile rounds, finish the rest with 128x128 tiles
@@ -780,7 +803,6 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   // round (<= one per CU, or close to two per CU everywhere, or K short enough that the uneven
   // share costs little) they beat splitting K over 256x256 tiles, whose partials cost HBM traffic
   // and a reduction.
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (t128 <= cus) {
     // At most one 128x128 tile per CU: splitting K over the idle CUs pays when the chunks saved
     // outweigh the fp32 partials and the reduction launch.  Cost model fit to a sweep (M 256 ..
@@ -847,6 +869,15 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         return launch_tiled<0, 128, 128, 2, 2, OUT, ABLK>(g, 0, (int)pl.n_big, M, N - (int)pl.n_big, 1, nullptr, stream);
       }
       return launch_tiled<0, 256, 256, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
+    case GemmVariant::W4A4_128x192: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<0, 128, 192, 2, 2, OUT, ABLK>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, g.a_ts, g.b_ts, g.qo, stream);
+      }
+      return launch_tiled<0, 128, 192, 2, 2, OUT, ABLK>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A4_128x128: {
       if (pl.splits > 1) {

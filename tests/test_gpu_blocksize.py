@@ -141,9 +141,15 @@ def test_gemm_w4a4_block_sizes(M, N, K, ba, bb):
 
 
 def test_gemm_w4a4_block_sizes_256_tiles_sampled():
-    """256x256 tiles (144 tiles, K = 1152) with 64-block activations and 32-block weights, on 96 x 96
+    """256x256 tiles (224 tiles, K = 1152) with 64-block activations and 32-block weights, on 96 x 96
     sampled outputs."""
-    run_w4a4_bs(4096, 2304, 1152, 64, 32, sample=(96, 96))
+    run_w4a4_bs(4096, 3456, 1152, 64, 32, sample=(96, 96))
+
+
+@pytest.mark.parametrize("ba,bb", [(64, 32), (32, 64)])
+def test_gemm_w4a4_block_sizes_128x192_tiles(ba, bb):
+    """128x192 tiles (204 tiles, ragged rows) with 32- and 64-block operands, every output."""
+    run_w4a4_bs(2100, 2304, 1152, ba, bb)
 
 
 @pytest.mark.parametrize("M,N,K,bb", [(100, 512, 512, 64), (8, 512, 1024, 32), (1, 2048, 3072, 64)])

@@ -176,7 +176,8 @@ def _strided_activation(x_cpu, b, lda):
     (300, 272, 1152, 32, 32),
     (300, 272, 1152, 64, 128),    # 64-blocks: byte positions shift with the row pitch
     (300, 272, 1152, 64, 64),
-    (4096, 1152, 1152, 16, 128),  # the PixArt proj shape with a padded activation
+    (4096, 1152, 1152, 16, 128),  # the PixArt proj shape (128 x 192 tiles) with a padded activation
+    (2100, 2304, 1152, 64, 128),  # 128 x 192 tiles, ragged rows, 64-blocks
     (512, 512, 4096, 64, 128),    # split-K plan
 ])
 def test_gemm_w4a4_strided_activation(M, N, K, b, pad):

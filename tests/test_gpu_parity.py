@@ -319,18 +319,37 @@ def test_gemm_w4a4_ragged(M, N, K):
     run_w4a4(x, w, torch.float32)
 
 
-@pytest.mark.parametrize("M,N,K", [
-    (512, 512, 4096),     # 16 tiles of 128 x 128, K split
-    (4096, 1024, 4096),   # 256 tiles of 128 x 128, one per CU
-    (2048, 4096, 1024),   # 512 tiles of 128 x 128, two per CU
-    (3072, 1408, 2048),   # 264 small tiles, uneven: 256 x 256 tiles with K split two ways
+@pytest.mark.parametrize("M,N,K,split", [
+    (512, 512, 4096, True),      # 16 tiles of 128 x 128, K split
+    (4096, 1024, 4096, False),   # 256 tiles of 128 x 128, one per CU
+    (2048, 4096, 1024, False),   # 512 tiles of 128 x 128, two per CU
+    (4096, 1664, 2048, True),    # 416 small tiles, 288 of 128 x 192: 256 x 256 tiles, K split two ways
+    (3072, 1408, 2048, False),   # 264 small tiles: 192 tiles of 128 x 192 (the last column 64 wide)
 ])
-def test_gemm_w4a4_planner_paths(M, N, K):
-    """One shape per plan of the W4A4 planner below one round of 256 x 256 tiles (sampled outputs)."""
+def test_gemm_w4a4_planner_paths(M, N, K, split):
+    """One shape per plan of the W4A4 planner below one round of 256 x 256 tiles (sampled outputs);
+    the workspace query says whether the plan splits K."""
+    assert (nv.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K) > 0) == split
     g = torch.Generator().manual_seed(M + N + K)
     x = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
     run_w4a4(x, w, torch.bfloat16, sample=(64, 64))
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    (2100, 2302, 1152, torch.bfloat16),  # ragged rows and columns; rows not 16-byte aligned (N % 8 != 0)
+    (2048, 2304, 1152, torch.float32),   # 192 tiles, one per CU
+    (4096, 2304, 1152, torch.float32),   # 384 tiles: two workgroups on half of the CUs
+])
+def test_gemm_w4a4_128x192_tiles(M, N, K, out_dtype):
+    """Every output of the W4A4 GEMM on shapes the planner gives 128 x 192 tiles (two 96-column wave
+    sub-tiles, stored as a 64- and a 32-column piece; two B scale units past the tile fetched and
+    unused)."""
+    assert nv.nvfp4_gemm_workspace_bytes(nv.W4A4, M, N, K) == 0
+    g = torch.Generator().manual_seed(M + 5 * N + K)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    run_w4a4(x, w, out_dtype)
 
 
 @pytest.mark.parametrize("M,N,K", [

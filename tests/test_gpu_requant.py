@@ -96,8 +96,10 @@ def run_requant(mode, M, N, K, bias_on, act, s_factor, seed, with_y=True):
 
 @pytest.mark.parametrize("M,N,K,bias_on,act,f", [
     (300, 272, 384, True, nv.ACT_GELU_TANH, 1.0),      # 128x128 tiles, ragged M
-    (4096, 2304, 256, False, nv.ACT_NONE, 0.25),       # 256x256 tiles, saturating scale
-    (4096, 4608, 128, True, nv.ACT_GELU_TANH, 1.0),    # 256x256 columns + 128x128 remainder
+    (4096, 2304, 256, False, nv.ACT_NONE, 0.25),       # 128x192 tiles, saturating scale
+    (4096, 3456, 256, False, nv.ACT_NONE, 1.0),        # 256x256 tiles (the last column half used)
+    (4096, 4608, 128, True, nv.ACT_GELU_TANH, 1.0),    # 128x192 tiles, three per CU
+    (4096, 5120, 128, True, nv.ACT_GELU_TANH, 1.0),    # 256x256 columns + 128x128 remainder
     (512, 512, 4096, True, nv.ACT_NONE, 3.7),          # split-K: the reduction requantizes
     (1, 64, 256, False, nv.ACT_NONE, 1.0),             # one row
     (64, 96, 48, True, nv.ACT_GELU_TANH, 1.0),         # generic kernel (K % 128 != 0)
