@@ -11,7 +11,7 @@
 // FP8; so the exact route is fp16 (W4A4) / bf16 (W4A16, where A is bf16) MFMA.
 //
 // Kernel structure (k_gemm_tiled): a 256-thread workgroup (4 waves) owns a BM x BN tile (W4A4:
-// 256 x 256, 128 x 128 or 128 x 192; W4A16: 128 x 256 or 256 x 256) and walks K in chunks of 128.
+// 256 x 256, 128 x 128 or 128 x 192; W4A16: 128 x 256) and walks K in chunks of 128.
 // Per chunk, LDS-DMA loads stage A codes + A scale bytes (or bf16 A) and one prepacked B unit per
 // 32 columns into a three-stage LDS ring, two chunks ahead of the MFMAs (one barrier per chunk).
 // Each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  For MFMA step s
@@ -30,16 +30,16 @@
 namespace nvfp4 {
 
 constexpr int kChunk = 128;  // k per LDS stage
-constexpr int64_t kW4A16TallM = 256;  // W4A16 rows from which 256-row tiles are considered
 constexpr bool kOutputNT = true;    // streaming stores for the bf16 / fp32 output
 constexpr bool kPartialNT = false;  // split-K partials (read back at once by the reduction)
 constexpr bool kReduceNT = false;   // the reduction reads the partials while they are still cached
 
-template <int MODE, int BM, int BN>
+// HS: W4A16 stages half chunks (64 k, one part of the prepacked units), so that a 128 x 256
+// workgroup's three stages take 78 KB of LDS and two workgroups fit on a CU.
+template <int MODE, int BM, int BN, bool HS>
 struct TileCfg {
-  // W4A16 with 256-row tiles stages half chunks (64 k, one part of the prepacked units): a whole
-  // chunk of bf16 A rows (64 KB) would leave room for only two stages
-  static constexpr bool kHalf = (MODE == 1 && BM == 256);
+  static_assert(!HS || MODE == 1, "half-chunk stages are a W4A16 form");
+  static constexpr bool kHalf = HS;
   static constexpr int kALds = (MODE == 0) ? BM * 64 : (kHalf ? BM * 128 : BM * 256);  // codes or bf16
   static constexpr int kASLds = (MODE == 0) ? BM * 8 : 0;
   static constexpr int kBLds = kHalf ? BN * 32 : BN * 64;
@@ -92,8 +92,8 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // LDS: a ring of three stages, the DMA two stages ahead of the MFMAs.  Stage layout:
 //   A codes   [BM/32][2 parts][64 lanes][16 B]   (MODE 0)  or  A bf16 [BM/32][8 steps][64 lanes][16 B]
 //   A scales  [BM/32][64 lanes][4 B]             (MODE 0)
-//   B codes   [BN/32][2 parts][64 lanes][16 B]   B scales [BN/32][64 lanes][4 B]
-// A stage is one 128-k chunk, except for W4A16 with 256-row tiles, whose stages are half chunks
+//   B codes   [BN/32][2 parts][64 lanes][16 B]   B scales [BN/32 rounded up to 4][64 lanes][4 B]
+// A stage is one 128-k chunk, except for W4A16 with half-chunk stages (HS)
 // (part p: A bf16 [BM/32][4 steps][64 lanes][16 B], B codes [BN/32][64 lanes][16 B]).
 // Each 1-KB (or 256-B) block is filled by one wave-wide LDS-DMA load whose lane addresses implement
 // the row-major -> lane-order permutation for A; B is prepacked in exactly this order.  Rows past
@@ -102,16 +102,18 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // ABLK: values per A scale byte along K (16, 32 or 64; W4A4).  Lane l = r + 32 h needs the bytes of
 // the blocks under its 64 k of a chunk: 4, 2 or 1 bytes, fetched as the aligned dword holding them
 // and shifted into place when read.
-template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK>
-// 128 x 128 and 128 x 192 tiles need few registers (64 / 96 accumulators per wave): two workgroups
-// per CU, so a grid a little larger than the CU count runs in one round; larger tiles one wave per
-// SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <= 128 * 192) ? 2 : 1, (BM * BN <= 128 * 192) ? 2 : 1))) void k_gemm_tiled(
+// Two workgroups per CU (a grid a little larger than the CU count runs in one round, and one wave's
+// VALU work runs beside the other's MFMAs): W4A4 128 x 128 and 128 x 192 tiles (64 / 96
+// accumulators per wave) and W4A16 128 x 256 tiles with half-chunk stages (128); larger tiles one
+// wave per SIMD.
+template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK, bool HS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    (BM * BN <= 128 * 192 || (HS && BM == 128)) ? 2 : 1, (BM * BN <= 128 * 192 || (HS && BM == 128)) ? 2 : 1))) void k_gemm_tiled(
     const void *__restrict__ a, const uint8_t *__restrict__ a_scales, const float *__restrict__ a_ts,
     const uint8_t *__restrict__ bp, const float *__restrict__ b_ts, int M, int N, int K, int64_t lda,
     void *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n, int m_off, int n_off, int splits,
     float *__restrict__ partial, QuantOut qo) {
-  using Cfg = TileCfg<MODE, BM, BN>;
+  using Cfg = TileCfg<MODE, BM, BN, HS>;
   constexpr int TM = BM / WM / 32;  // MFMA tiles per wave along M
   constexpr int TN = BN / WN / 32;
   constexpr bool HALF = Cfg::kHalf;
@@ -404,10 +406,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((BM * BN <=
     chunk(0, std::true_type{});
     for (int kc = 1; kc < nk; ++kc) chunk(kc, std::false_type{});
   } else if constexpr (HALF) {
-    // ---- W4A16, 256-row tiles: half-chunk stages (part p of each chunk: its 4 MFMA steps); per
-    // stage the wave's B codes and scales into registers, the DMA of stage g + 2 into the third
-    // buffer, then 4 steps with the next step's B dequantization and A reads pipelined beside the
-    // current step's MFMAs.  Each dequantized B fragment feeds TM = 8 MFMAs. ----
+    // ---- W4A16, half-chunk stages (part p of each chunk: its 4 MFMA steps); per stage the wave's
+    // B codes and scales into registers, the DMA of stage g + 2 into the third buffer, then 4 steps
+    // with the next step's B dequantization and A reads pipelined beside the current step's MFMAs.
+    // Each dequantized B fragment feeds TM = 4 MFMAs. ----
     const int ng = 2 * (kend - kbeg);
     issue(2 * kbeg, 0);
     if (ng > 1) {
@@ -693,12 +695,12 @@ hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int
 
 // ---- launchers ----------------------------------------------------------------------------------
 
-template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK = 16>
+template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK = 16, bool HS = false>
 static hipError_t launch_tiled(const GemmArgs &g, int m_off, int n_off, int m_len, int n_len, int splits,
                                float *partial, hipStream_t stream) {
-  using Cfg = TileCfg<MODE, BM, BN>;
+  using Cfg = TileCfg<MODE, BM, BN, HS>;
   const int tm = (m_len + BM - 1) / BM, tn = (n_len + BN - 1) / BN;
-  auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT, ABLK>;
+  auto kern = k_gemm_tiled<MODE, BM, BN, WM, WN, OUT, ABLK, HS>;
   const int smem = 3 * Cfg::kStage;
   static std::atomic<bool> configured[kMaxDevices];  // per instantiation and device
   hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), smem, configured);
@@ -720,9 +722,9 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Plan: which tile kernel(s) (W4A4: 256x256, 128x192 or 128x128; W4A16: 128x256, 256x256 or the
-// skinny kernel), how many K splits, and an optional split of N into a region of 256x256 tiles
-// (exactly one round on the chip) plus a remainder of 128x128 tiles.
+// Plan: which tile kernel(s) (W4A4: 256x256, 128x192 or 128x128; W4A16: 128x256 with whole- or
+// half-chunk stages, or the skinny kernel), how many K splits, and an optional split of N into a
+// region of 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   GemmPlan pl;
   const int64_t arow_bytes = (mode == 0) ? lda / 2 : lda * 2;
@@ -748,24 +750,30 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
       pl.waves = per >= 48 ? 16 : (per >= 16 ? 8 : 4);
       return pl;
     }
-    // 128 x 256 or 256 x 256 tiles (the latter reuse each dequantized B fragment for 8 MFMAs instead
-    // of 4) and a K split, by a cost model fit to measurements (M 64..4096, N and K 1024..12288):
-    // rounds of workgroups x chunks per split x a chunk's time for the tile, plus the fp32 partials'
-    // traffic (written, read back, output written) of a split.  Splits keep >= 6 chunks each.
+    // 128 x 256 tiles, with whole-chunk stages (one workgroup per CU) or half-chunk stages (two
+    // workgroups per CU: one wave's dequantization runs beside the other's MFMAs), and a K split, by
+    // a cost model fit to measurements (M 64..4096, N and K 1024..12288; the two-per-CU form on a
+    // sweep of 30 shapes, M 128..4096 over five N x K pairs, where it picks a plan within 5 % of
+    // the fastest measured on 29): chunks per split x a chunk's time for the form and the
+    // workgroups a CU runs (whole-chunk stages: 1.99 us per workgroup, one at a time; half-chunk
+    // stages: 3.5 us for two sharing a CU, 2.2 us for one alone), plus the fp32 partials' traffic
+    // (written, read back, output written) of a split.  Splits keep >= 6 chunks each.  The
+    // two-per-CU form replaced 256 x 256 tiles (one per CU, 3.71 us a chunk), which it beat on every
+    // shape measured: up projection N 12288, K 3072 at M = 1024 103 -> 82 us, 4096 308 -> 268 us;
+    // down (N 3072, K 12288) at M = 4096 331 -> 300 us.
     double best_t = 1e300;
-    for (int cfg = 0; cfg < 2; ++cfg) {
-      if (cfg == 1 && M < kW4A16TallM) continue;
-      const int64_t bm = cfg ? 256 : 128;
-      const double chunk_us = cfg ? 3.71 : 1.99;
-      const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
+    for (int half = 0; half < 2; ++half) {
+      const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
       for (int sp = 1; sp <= 16; ++sp) {
         if (sp > 1 && (Kc / sp < 6 || N % 4 != 0)) continue;
-        const double rounds = (double)((tiles * sp + cus - 1) / cus);
-        double t = rounds * (double)((Kc + sp - 1) / sp) * chunk_us;
+        const int64_t per_cu = (tiles * sp + cus - 1) / cus;  // workgroups per CU, rounded up
+        const double chunks = (double)((Kc + sp - 1) / sp);
+        double t = half ? chunks * ((double)(per_cu / 2) * 3.5 + (double)(per_cu % 2) * 2.2)
+                        : chunks * (double)per_cu * 1.99;
         if (sp > 1) t += (8.0 * sp + 2.0) * (double)M * (double)N / 5.19e6;
         if (t < best_t) {
           best_t = t;
-          pl.variant = cfg ? GemmVariant::W4A16_256x256 : GemmVariant::W4A16_128x256;
+          pl.variant = half ? GemmVariant::W4A16_128x256h : GemmVariant::W4A16_128x256;
           pl.splits = sp;
         }
       }
@@ -897,14 +905,14 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
       }
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
     }
-    case GemmVariant::W4A16_256x256: {
+    case GemmVariant::W4A16_128x256h: {
       if (pl.splits > 1) {
         float *part = static_cast<float *>(g.workspace);
-        hipError_t e = launch_tiled<1, 256, 256, 1, 4, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        hipError_t e = launch_tiled<1, 128, 256, 1, 4, OUT, 16, true>(g, 0, 0, M, N, pl.splits, part, stream);
         if (e != hipSuccess) return e;
         return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
       }
-      return launch_tiled<1, 256, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+      return launch_tiled<1, 128, 256, 1, 4, OUT, 16, true>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A16_Skinny:
       return launch_gemm_skinny(g, pl.waves, pl.splits, static_cast<float *>(g.workspace), stream);

@@ -152,7 +152,8 @@ def test_gemm_w4a4_block_sizes_128x192_tiles(ba, bb):
     run_w4a4_bs(2100, 2304, 1152, ba, bb)
 
 
-@pytest.mark.parametrize("M,N,K,bb", [(100, 512, 512, 64), (8, 512, 1024, 32), (1, 2048, 3072, 64)])
+@pytest.mark.parametrize("M,N,K,bb", [(100, 512, 512, 64), (8, 512, 1024, 32), (1, 2048, 3072, 64),
+                                      (3000, 2608, 384, 32)])  # half-chunk stages, two per CU
 def test_gemm_w4a16_block_sizes(M, N, K, bb):
     say(f"[gemm W4A16] M={M} N={N} K={K} B block {bb}")
     g = torch.Generator().manual_seed(M + N + K + bb)

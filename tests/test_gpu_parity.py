@@ -421,8 +421,10 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
                                    (33, 1000, 2048), (48, 130, 1152), (64, 4096, 3072),
                                    # tiled kernel with K split
                                    (200, 520, 2048),
-                                   # 256-row tiles (half-chunk stages): ragged M and N, K split, 9 chunks
-                                   (600, 520, 384), (512, 256, 4096), (1000, 300, 1152)])
+                                   # 128 x 256 tiles, whole-chunk stages: ragged M and N, K split, 9 chunks
+                                   (600, 520, 384), (512, 256, 4096), (1000, 300, 1152),
+                                   # half-chunk stages, two workgroups per CU: ragged, K split 7 / 3 ways
+                                   (3000, 2600, 384), (4100, 300, 12288), (1500, 2600, 4096)])
 def test_gemm_w4a16_ragged(M, N, K):
     g = torch.Generator().manual_seed(M * 5 + N + K)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
@@ -430,11 +432,12 @@ def test_gemm_w4a16_ragged(M, N, K):
     run_w4a16(a, w, torch.float32)
 
 
-@pytest.mark.parametrize("M", [1, 9, 17, 32, 50, 300])
-def test_gemm_w4a16_strided_activation(M):
+@pytest.mark.parametrize("M,N,K", [(1, 520, 1152), (9, 520, 1152), (17, 520, 1152), (32, 520, 1152),
+                                   (50, 520, 1152), (300, 520, 1152), (3000, 2600, 384)])
+def test_gemm_w4a16_strided_activation(M, N, K):
     """A row-strided activation view (lda = K + 64, the padding holds 1e30 and must be ignored):
-    streaming kernel for each row class, tiled kernel for M = 300."""
-    N, K = 520, 1152
+    streaming kernel for each row class, tiled kernel for M = 300 (whole-chunk stages) and M = 3000
+    (half-chunk stages, two workgroups per CU)."""
     g = torch.Generator().manual_seed(900 + M)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = workloads.laplace_tailed_weight(N, K, g)
