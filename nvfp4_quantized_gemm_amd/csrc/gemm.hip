@@ -11,7 +11,7 @@
 // FP8; so the exact route is fp16 (W4A4) / bf16 (W4A16, where A is bf16) MFMA.
 //
 // Kernel structure (k_gemm_tiled): a 256-thread workgroup (4 waves) owns a BM x BN tile (W4A4:
-// 256 x 256, 128 x 128 or 128 x 192; W4A16: 128 x 256) and walks K in chunks of 128.
+// 256 x 256, 128 x 128 or 128 x 192; W4A16: 128 x 256 or 64 x 256) and walks K in chunks of 128.
 // Per chunk, LDS-DMA loads stage A codes + A scale bytes (or bf16 A) and one prepacked B unit per
 // 32 columns into a three-stage LDS ring, two chunks ahead of the MFMAs (one barrier per chunk).
 // Each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  For MFMA step s
@@ -723,7 +723,7 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
 }
 
 // Plan: which tile kernel(s) (W4A4: 256x256, 128x192 or 128x128; W4A16: 128x256 with whole- or
-// half-chunk stages, or the skinny kernel), how many K splits, and an optional split of N into a
+// half-chunk stages, 64x256, or the skinny kernel), how many K splits, and an optional split of N into a
 // region of 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   GemmPlan pl;
@@ -750,30 +750,34 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
       pl.waves = per >= 48 ? 16 : (per >= 16 ? 8 : 4);
       return pl;
     }
-    // 128 x 256 tiles, with whole-chunk stages (one workgroup per CU) or half-chunk stages (two
-    // workgroups per CU: one wave's dequantization runs beside the other's MFMAs), and a K split, by
-    // a cost model fit to measurements (M 64..4096, N and K 1024..12288; the two-per-CU form on a
-    // sweep of 30 shapes, M 128..4096 over five N x K pairs, where it picks a plan within 5 % of
-    // the fastest measured on 29): chunks per split x a chunk's time for the form and the
-    // workgroups a CU runs (whole-chunk stages: 1.99 us per workgroup, one at a time; half-chunk
-    // stages: 3.5 us for two sharing a CU, 2.2 us for one alone), plus the fp32 partials' traffic
-    // (written, read back, output written) of a split.  Splits keep >= 6 chunks each.  The
-    // two-per-CU form replaced 256 x 256 tiles (one per CU, 3.71 us a chunk), which it beat on every
-    // shape measured: up projection N 12288, K 3072 at M = 1024 103 -> 82 us, 4096 308 -> 268 us;
-    // down (N 3072, K 12288) at M = 4096 331 -> 300 us.
+    // Tiles of 128 x 256 with whole-chunk stages (one workgroup per CU) or half-chunk stages (two
+    // workgroups per CU: one wave's dequantization runs beside the other's MFMAs), or of 64 x 256
+    // (twice the dequantization per MFMA, but twice the workgroups before K has to be split), and a
+    // K split, by a cost model fit to measurements (M 64..4096, N and K 1024..12288; the two-per-CU
+    // form on a sweep of 30 shapes, M 128..4096, and the 64-row form on 30 more, M 96..768, over
+    // five N x K pairs): chunks per split x a chunk's time for the form and the workgroups a CU runs
+    // (whole-chunk 128 x 256: 1.99 us per workgroup, one at a time; half-chunk: 3.5 us for two
+    // sharing a CU, 2.2 us for one alone; 64 x 256: 1.5 us, one at a time), plus, for a split, the
+    // fp32 partials' traffic (written, read back, output written) and the reduction's launch.
+    // Splits keep >= 6 chunks each.  Against the one-per-CU forms alone: up projection N 12288, K
+    // 3072 at M = 256 43 -> 40 us, 1024 103 -> 82 us, 4096 308 -> 268 us; down (N 3072, K 12288)
+    // at M = 4096 331 -> 300 us; N 1024 / 4096 / 8192 at M <= 512 by 10-27 %.  (256 x 256 tiles,
+    // one per CU at 3.71 us a chunk, were slower than the two-per-CU form on every shape measured.)
     double best_t = 1e300;
-    for (int half = 0; half < 2; ++half) {
-      const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    for (int form = 0; form < 3; ++form) {
+      const int64_t bm = form == 2 ? 64 : 128;
+      const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
       for (int sp = 1; sp <= 16; ++sp) {
         if (sp > 1 && (Kc / sp < 6 || N % 4 != 0)) continue;
         const int64_t per_cu = (tiles * sp + cus - 1) / cus;  // workgroups per CU, rounded up
         const double chunks = (double)((Kc + sp - 1) / sp);
-        double t = half ? chunks * ((double)(per_cu / 2) * 3.5 + (double)(per_cu % 2) * 2.2)
-                        : chunks * (double)per_cu * 1.99;
-        if (sp > 1) t += (8.0 * sp + 2.0) * (double)M * (double)N / 5.19e6;
+        double t = form == 1 ? chunks * ((double)(per_cu / 2) * 3.5 + (double)(per_cu % 2) * 2.2)
+                             : chunks * (double)per_cu * (form == 2 ? 1.5 : 1.99);
+        if (sp > 1) t += (8.0 * sp + 2.0) * (double)M * (double)N / 5.19e6 + 3.0;
         if (t < best_t) {
           best_t = t;
-          pl.variant = half ? GemmVariant::W4A16_128x256h : GemmVariant::W4A16_128x256;
+          pl.variant = form == 0 ? GemmVariant::W4A16_128x256
+                                 : (form == 1 ? GemmVariant::W4A16_128x256h : GemmVariant::W4A16_64x256);
           pl.splits = sp;
         }
       }
@@ -904,6 +908,15 @@ static hipError_t run_plan(const GemmArgs &g, const GemmPlan &pl, hipStream_t st
         return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
       }
       return launch_tiled<1, 128, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
+    }
+    case GemmVariant::W4A16_64x256: {
+      if (pl.splits > 1) {
+        float *part = static_cast<float *>(g.workspace);
+        hipError_t e = launch_tiled<1, 64, 256, 1, 4, OUT>(g, 0, 0, M, N, pl.splits, part, stream);
+        if (e != hipSuccess) return e;
+        return launch_splitk_reduce(part, pl.splits, M, N, g.c, OUT, g.ldc, nullptr, g.b_ts, g.qo, stream);
+      }
+      return launch_tiled<1, 64, 256, 1, 4, OUT>(g, 0, 0, M, N, 1, nullptr, stream);
     }
     case GemmVariant::W4A16_128x256h: {
       if (pl.splits > 1) {

@@ -56,8 +56,10 @@ hipError_t launch_prepack(const uint8_t *packed, const uint8_t *scales, int64_t 
 hipError_t launch_unpack(const void *in, int64_t N, int64_t K, int blk, uint8_t *packed, uint8_t *scales,
                          hipStream_t stream);
 
-// W4A16_128x256h: 128 x 256 tiles with half-chunk stages, two workgroups per CU
-enum class GemmVariant { Generic, W4A4_256x256, W4A4_128x128, W4A4_128x192, W4A16_128x256, W4A16_128x256h, W4A16_Skinny };
+// W4A16_128x256h: 128 x 256 tiles with half-chunk stages, two workgroups per CU; W4A16_64x256: 64-row tiles
+enum class GemmVariant {
+  Generic, W4A4_256x256, W4A4_128x128, W4A4_128x192, W4A16_128x256, W4A16_128x256h, W4A16_64x256, W4A16_Skinny
+};
 
 struct GemmPlan {
   GemmVariant variant = GemmVariant::Generic;

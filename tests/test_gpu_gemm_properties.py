@@ -1,8 +1,8 @@
 """GPU property tests of the GEMMs over shapes: Hypothesis draws M, N, K (whole 128-k chunks or
 not, ragged tile edges, one row to a few thousand), the mode (W4A4 at block sizes 16 / 32 / 64,
 W4A16, MXFP4) and the output type, so the planners' every plan is reached (256x256, 128x192 and
-128x128 tiles, the mixed plan, K splits, both W4A16 stage forms, the streaming kernel's row classes
-and splits, the generic kernel).
+128x128 tiles, the mixed plan, K splits, the three W4A16 tile forms, the streaming kernel's row
+classes and splits, the generic kernel).
 Each case compares sampled output rows and columns with the oracle's dequantize-then-fp64-matmul
 of the oracle's own quantization: within 1e-5 sum|a b| per element (fp32 output), plus the bf16
 rounding for bf16 output [NVFP4-DiT page, Methodology section 3; vllm-omni NVFP4 RFC, Open
@@ -51,9 +51,10 @@ def gemm_case(draw):
 @example(("w4a4", 4096, 5120, 1024, torch.bfloat16, 23))    # one round of 256 tiles + 128 tiles
 @example(("w4a4_b64", 8192, 4608, 1024, torch.float32, 24))  # 2.25 rounds of 256x256 tiles
 @example(("w4a4", 4096, 1664, 2048, torch.bfloat16, 25))    # 256x256 tiles, two-way K split
-@example(("w4a16", 1024, 3072, 3072, torch.bfloat16, 15))   # 128x256 W4A16 tiles, whole-chunk stages, K split
-@example(("w4a16", 300, 12288, 3072, torch.float32, 16))    # half-chunk stages, two per CU, K split
+@example(("w4a16", 2100, 300, 4096, torch.bfloat16, 15))    # 128x256 W4A16 tiles, whole-chunk stages, K split
+@example(("w4a16", 1500, 2600, 4096, torch.float32, 16))    # half-chunk stages, two per CU, K split
 @example(("w4a16", 3000, 2600, 384, torch.bfloat16, 26))    # half-chunk stages, unsplit, ragged
+@example(("w4a16", 300, 12288, 3072, torch.float32, 27))    # 64x256 W4A16 tiles
 @example(("w4a16", 16, 512, 4096, torch.float32, 17))       # streaming kernel, K split
 @example(("w4a16", 32, 3072, 12288, torch.bfloat16, 18))    # streaming kernel, 32 rows
 @example(("w4a16", 57, 12288, 3072, torch.bfloat16, 22))    # streaming kernel, two row groups

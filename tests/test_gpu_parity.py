@@ -419,10 +419,10 @@ def run_w4a16(a_cpu, w_cpu, out_dtype, sample=None):
                                    (4, 520, 1152), (9, 300, 1152), (17, 1000, 2048), (32, 4096, 3072),
                                    # two row groups (33..64 rows)
                                    (33, 1000, 2048), (48, 130, 1152), (64, 4096, 3072),
-                                   # tiled kernel with K split
-                                   (200, 520, 2048),
-                                   # 128 x 256 tiles, whole-chunk stages: ragged M and N, K split, 9 chunks
-                                   (600, 520, 384), (512, 256, 4096), (1000, 300, 1152),
+                                   # 64 x 256 tiles: K split two / five ways, ragged M and N, 9 chunks
+                                   (200, 520, 2048), (600, 520, 384), (512, 256, 4096), (1000, 300, 1152),
+                                   # 128 x 256 tiles, whole-chunk stages: ragged, K split five ways
+                                   (1500, 2600, 384), (2100, 300, 4096),
                                    # half-chunk stages, two workgroups per CU: ragged, K split 7 / 3 ways
                                    (3000, 2600, 384), (4100, 300, 12288), (1500, 2600, 4096)])
 def test_gemm_w4a16_ragged(M, N, K):
@@ -433,11 +433,11 @@ def test_gemm_w4a16_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 520, 1152), (9, 520, 1152), (17, 520, 1152), (32, 520, 1152),
-                                   (50, 520, 1152), (300, 520, 1152), (3000, 2600, 384)])
+                                   (50, 520, 1152), (300, 520, 1152), (1500, 2600, 384), (3000, 2600, 384)])
 def test_gemm_w4a16_strided_activation(M, N, K):
     """A row-strided activation view (lda = K + 64, the padding holds 1e30 and must be ignored):
-    streaming kernel for each row class, tiled kernel for M = 300 (whole-chunk stages) and M = 3000
-    (half-chunk stages, two workgroups per CU)."""
+    streaming kernel for each row class, then the tiled forms: 64 x 256 tiles (M = 300), 128 x 256
+    with whole-chunk stages (M = 1500) and with half-chunk stages, two workgroups per CU (M = 3000)."""
     g = torch.Generator().manual_seed(900 + M)
     a = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = workloads.laplace_tailed_weight(N, K, g)
