@@ -105,7 +105,8 @@ __device__ __forceinline__ void store_out(void *c, int64_t ldc, int64_t row, int
 // Two workgroups per CU (a grid a little larger than the CU count runs in one round, and one wave's
 // VALU work runs beside the other's MFMAs): W4A4 128 x 128 and 128 x 192 tiles (64 / 96
 // accumulators per wave) and W4A16 128 x 256 tiles with half-chunk stages (128); larger tiles one
-// wave per SIMD.
+// wave per SIMD.  (W4A16 64 x 256 tiles get the same register budget, but their three whole-chunk
+// stages, 102 KB of LDS, leave room for one workgroup per CU.)
 template <int MODE, int BM, int BN, int WM, int WN, int OUT, int ABLK, bool HS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     (BM * BN <= 128 * 192 || (HS && BM == 128)) ? 2 : 1, (BM * BN <= 128 * 192 || (HS && BM == 128)) ? 2 : 1))) void k_gemm_tiled(
@@ -723,8 +724,8 @@ static hipError_t launch_generic(const GemmArgs &g, hipStream_t stream) {
 }
 
 // Plan: which tile kernel(s) (W4A4: 256x256, 128x192 or 128x128; W4A16: 128x256 with whole- or
-// half-chunk stages, 64x256, or the skinny kernel), how many K splits, and an optional split of N into a
-// region of 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
+// half-chunk stages, 64x256, or the skinny kernel), how many K splits, and an optional split of N
+// into a region of 256x256 tiles (exactly one round on the chip) plus a remainder of 128x128 tiles.
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
   GemmPlan pl;
   const int64_t arow_bytes = (mode == 0) ? lda / 2 : lda * 2;
@@ -733,7 +734,7 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K, int64_t lda) {
     pl.variant = GemmVariant::Generic;
     return pl;
   }
-  const int64_t cus = 256;  // planning for the MI355X chip (one workgroup of either tile per CU)
+  const int64_t cus = 256;  // planning for the MI355X chip (256 CUs)
   const int64_t Kc = K / kChunk;
   if (mode == 1) {
     const int64_t Nu = (N + 31) / 32;

@@ -113,6 +113,8 @@ def test_requant_w4a4(M, N, K, bias_on, act, f):
 @pytest.mark.parametrize("M,N,K,bias_on,act,f", [
     (100, 512, 512, False, nv.ACT_GELU_TANH, 1.0),     # W4A16 64x256 tiles
     (1500, 2608, 384, False, nv.ACT_NONE, 1.0),        # 128x256 tiles, whole-chunk stages
+    (300, 1008, 2048, True, nv.ACT_GELU_TANH, 1.0),    # 64x256 tiles, K split: the reduction requantizes
+    (2100, 304, 4096, False, nv.ACT_NONE, 0.25),       # 128x256 tiles, K split five ways, saturating
     (3000, 2608, 384, True, nv.ACT_GELU_TANH, 1.0),    # half-chunk stages, two workgroups per CU
     (8, 512, 1024, True, nv.ACT_GELU_TANH, 1.0),       # skinny rows, fp32 pass then requantize
     (1, 2048, 12288, True, nv.ACT_NONE, 0.5),          # skinny, one row, split K
