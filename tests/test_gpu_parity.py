@@ -457,9 +457,10 @@ def test_gemm_w4a16_strided_activation(M, N, K):
 
 
 def test_gemm_w4a16_full_size():
+    """The weight-only up and down projections at M = 1, 16, 256 and 4096, every output element."""
     for name, (w, acts) in workloads.w4a16().items():
         for m, a in acts.items():
-            run_w4a16(a, w, torch.bfloat16, sample=None if m <= 16 else 64)
+            run_w4a16(a, w, torch.bfloat16)
 
 
 def test_empty_tensors():
