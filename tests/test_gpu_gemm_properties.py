@@ -102,3 +102,81 @@ def test_gemm_shapes_against_oracle(case):
     Y, R = oracle.gemm(A, B)
     Yg = y.float().cpu().numpy()[np.ix_(rows, cols)]
     check_gemm(Yg, Y, R, out_dtype == torch.bfloat16, f"{mode} {M}x{N}x{K}")
+
+
+@st.composite
+def requant_case(draw):
+    mode = draw(st.sampled_from(["w4a4", "w4a4_b32", "w4a4_b64", "w4a16"]))
+    M = draw(st.one_of(st.integers(1, 70), st.integers(71, 2100)))
+    N = 16 * draw(st.integers(1, 150))
+    kb = 64 if mode == "w4a4_b64" else (32 if mode == "w4a4_b32" else 16)
+    K = 128 * draw(st.integers(1, 24)) if draw(st.booleans()) else kb * draw(st.integers(1, 60))
+    pad = draw(st.sampled_from([0, 128, kb]))
+    act = draw(st.sampled_from([nv.ACT_NONE, nv.ACT_GELU_TANH]))
+    s_factor = draw(st.sampled_from([0.25, 1.0, 4.0]))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    return mode, M, N, K, pad, act, s_factor, seed
+
+
+@SETTINGS
+@given(requant_case())
+@example(("w4a4", 2100, 2304, 1152, 128, nv.ACT_GELU_TANH, 1.0, 31))   # 128x192 tiles, strided A
+@example(("w4a16", 1500, 2608, 384, 16, nv.ACT_NONE, 0.25, 32))         # 128x256 W4A16 tiles, strided A
+@example(("w4a4_b64", 512, 512, 4096, 64, nv.ACT_GELU_TANH, 4.0, 33))  # K split, generic pitch
+def test_gemm_requant_strided_shapes_against_oracle(case):
+    """The NVFP4-output GEMM (bias, optional tanh GELU, static output scale) on drawn shapes, block
+    sizes and row-strided activations (a pitch of K + 128 keeps the tiled plans, K + block size runs
+    the generic kernel): the fp32 values on sampled rows and columns within the GEMM bar plus the
+    epilogue's rounding, and every NVFP4 byte equal to the oracle's quantization of the GPU's own
+    fp32 values [NVFP4-DiT page, Methodology section 3 and Definition III.1]."""
+    mode, M, N, K, pad, act, s_factor, seed = case
+    bb = 64 if mode == "w4a4_b64" else (32 if mode == "w4a4_b32" else 16)
+    lda = K + pad
+    say(f"[requant property] {mode} M={M} N={N} K={K} lda={lda} act={act} seed={seed}")
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    bias = (0.5 * torch.randn(N, generator=g)).to(torch.float32)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 16), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, N, 16), [0, N - 1]]))
+    xo, wo = np_x(x), np_x(w)
+    wp, ws, wS = nv.nvfp4_quantize(w.to(DEV), block_size=bb)
+    bp = nv.nvfp4_prepack_weight(wp, ws)
+    SB = oracle.tensor_scale(wo)
+    bo_p, bo_s, _ = oracle.quantize(np.ascontiguousarray(wo[cols]), S=SB, block=bb)
+    B, _ = oracle.dequantize(bo_p, bo_s, SB)
+    if mode == "w4a16":
+        big = torch.full((M, lda), 1e30, dtype=torch.bfloat16)
+        big[:, :K] = x
+        a_args = (big.to(DEV)[:, :K], None, None)
+        A = oracle.bf16_to_f32(xo[rows])
+        gmode = nv.W4A16
+    else:
+        pa, sa, Sa = nv.nvfp4_quantize(x.to(DEV), block_size=bb)
+        if pad:  # rows of lda values whose padding holds codes 0xF and scale bytes 448
+            big_p = torch.full((M, lda // 2), 0xFF, dtype=torch.uint8, device=DEV)
+            big_s = torch.full((M, lda // bb), 0x7E, dtype=torch.uint8, device=DEV)
+            big_p[:, : K // 2] = pa
+            big_s[:, : K // bb] = sa
+            pa, sa = big_p[:, : K // 2], big_s[:, : K // bb]
+        a_args = (pa, sa, Sa)
+        SA = oracle.tensor_scale(xo)
+        ap, as_, _ = oracle.quantize(np.ascontiguousarray(xo[rows]), S=SA, block=bb)
+        A, _ = oracle.dequantize(ap, as_, SA)
+        gmode = nv.W4A4
+    Y, R = oracle.gemm(A, B)
+    z = Y + bias.numpy().astype(np.float64)[cols][None, :]
+    yref = oracle.linear_epilogue(Y, bias.numpy()[cols], act)
+    S_out = np.float32(max(float(np.max(np.abs(yref))), 1e-30) / 2688.0 * s_factor)
+    So = torch.tensor([float(S_out)], dtype=torch.float32, device=DEV)
+    yf = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    hp, hs = nv.nvfp4_gemm_requant(gmode, *a_args, bp, wS, N, K, So, bias=bias.to(DEV), act=act, y=yf)
+    torch.cuda.synchronize()
+    yg = yf.cpu().numpy()
+    err = np.abs(yg[np.ix_(rows, cols)].astype(np.float64) - yref)
+    tol = 1.2e-5 * R + 5e-7 * np.abs(z) + 1e-30
+    assert (err <= tol).all(), f"{int((err > tol).sum())} fp32 values outside tolerance"
+    op, os_, _ = oracle.quantize(np.ascontiguousarray(yg), S=S_out)
+    assert np.array_equal(hs.cpu().numpy(), os_), "scale bytes differ"
+    assert np.array_equal(hp.cpu().numpy(), op), "code bytes differ"
