@@ -28,8 +28,11 @@
  *   - Shape, stride, alignment, dtype, mode and workspace checks run on the host before any HIP
  *     call; on failure the call returns the status and launches nothing.
  *   - After launching, a HIP error is reported as NVFP4_ERR_HIP.
- *   - Preconditions on device data are not checked: finite inputs; a static S that is finite
- *     and > 0; scale bytes never 0x7F/0xFF.  Results are undefined when they fail.
+ *   - Preconditions on device data (finite inputs and bias; tensor scales finite, and > 0 where
+ *     the call divides by one: a STATIC quantize S and the requantizing GEMM's output S; E4M3
+ *     scale bytes never 0x7F/0xFF, E8M0 scale bytes never 0xFF) are not checked by default, and
+ *     results are undefined when they fail.  Debug checks (nvfp4_set_debug_checks below) scan
+ *     them on the device before each call's launches.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -41,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 typedef enum {
   NVFP4_OK = 0,
@@ -54,6 +57,7 @@ typedef enum {
   NVFP4_ERR_WORKSPACE = 7, /* workspace required but NULL or smaller than the query says */
   NVFP4_ERR_HIP = 8,       /* a HIP runtime call or kernel launch failed */
   NVFP4_ERR_DEVICE = 9,    /* the current device is not a gfx950 GPU */
+  NVFP4_ERR_PRECONDITION = 10, /* debug checks on: device data the call would read breaks a precondition */
   /* Range sentinels (not statuses): they give every enum of this header the full range of int, so
      any int a caller passes -- including an invalid one, which the calls reject -- is a value of
      the type on both sides of the C / C++ boundary. */
@@ -81,6 +85,33 @@ const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* NVFP4_ABI_VERSION of the built library. */
 int nvfp4_abi_version(void);
+
+/* Debug checks of the preconditions on device data (off by default; diagnosis, not speed).
+ *
+ * When on, every call that passes its host-side checks first scans, on its stream, exactly the
+ * device data it is about to read, waits for the stream, and returns NVFP4_ERR_PRECONDITION --
+ * with nothing else launched and no output written -- if any value breaks the preconditions
+ * stated above:
+ *   quantize, fake quantize, MX quantize   every element of the logical [M][K] input finite;
+ *                                          STATIC: S finite and > 0
+ *   dequantize                             scale bytes not NaN; S finite
+ *   prepack                                scale bytes not NaN
+ *   GEMM, requantizing GEMM                W4A4: the [M][K/block] activation scale bytes not NaN,
+ *                                          S_A finite; W4A16: the [M][K] bf16 activation finite;
+ *                                          the prepacked weight's scale bytes not NaN, S_B finite;
+ *                                          requantizing: bias finite, output S finite and > 0
+ *   MX dequantize, MX GEMM                 E8M0 scale bytes not 0xFF
+ * (unpack reads only bytes and is not scanned).  The wait makes every call synchronous.  A stream
+ * under graph capture cannot be waited on, so captured calls skip the scans.  The scans use a
+ * library-owned flag word per call in flight (64 of them, taken round-robin per device): more than
+ * 64 calls scanning at once on one device may see each other's violations.
+ *
+ * The initial setting is read from the environment variable NVFP4_DEBUG when a call first needs
+ * it: set and not "0" turns the checks on.  nvfp4_set_debug_checks(enable) then turns them on
+ * (enable != 0) or off for every later call of the process, and returns the previous setting
+ * (1 on, 0 off).  Setting it while calls on other host threads are being validated is not ordered
+ * with those calls. */
+int nvfp4_set_debug_checks(int enable);
 
 /* ---------------------------------------------------------------------------------------------
  * Quantize [NVFP4-DiT page, Definition III.1; vllm-omni RFC, Motivation].

@@ -28,6 +28,7 @@ class Status(IntEnum):
     ERR_WORKSPACE = 7
     ERR_HIP = 8
     ERR_DEVICE = 9
+    ERR_PRECONDITION = 10
 
 
 F32, BF16 = 0, 1
@@ -44,7 +45,7 @@ EXPORTED = (
     "nvfp4_quantize_bs", "nvfp4_dequantize_bs", "nvfp4_fake_quantize_bs", "nvfp4_prepack_weight_bs",
     "nvfp4_unpack_weight_bs", "nvfp4_gemm_bs", "nvfp4_gemm_requant_bs",
     "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
-    "nvfp4_quantize_noalloc",
+    "nvfp4_quantize_noalloc", "nvfp4_set_debug_checks",
 )
 
 _lib = None
@@ -70,6 +71,8 @@ def lib():
     L.nvfp4_status_string.argtypes = [_i]
     L.nvfp4_abi_version.restype = _i
     L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_set_debug_checks.restype = _i
+    L.nvfp4_set_debug_checks.argtypes = [_i]
     L.nvfp4_quantize_workspace_bytes.restype = _sz
     L.nvfp4_quantize_workspace_bytes.argtypes = [_i64, _i64]
     L.nvfp4_quantize.restype = _i
@@ -145,6 +148,14 @@ def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return BF16
     raise TypeError(f"unsupported dtype {dt}; libnvfp4 takes float32 or bfloat16")
+
+
+def nvfp4_set_debug_checks(enable: bool) -> bool:
+    """Turn the library's device-data precondition scans on or off for every later call; returns
+    the previous setting.  When on, a call whose inputs hold a non-finite value, a NaN scale byte
+    or an invalid tensor scale raises NVFP4Error(ERR_PRECONDITION) and launches nothing; every call
+    then waits on its stream.  The initial setting comes from the NVFP4_DEBUG environment variable."""
+    return bool(lib().nvfp4_set_debug_checks(1 if enable else 0))
 
 
 def _rows(t: torch.Tensor, name: str):
@@ -423,7 +434,7 @@ def nvfp4_mx_gemm(a: torch.Tensor, a_scales: torch.Tensor, b: torch.Tensor, b_sc
 
 __all__ = [
     "Status", "NVFP4Error", "lib", "LIB_PATH", "EXPORTED", "F32", "BF16", "W4A4", "W4A16",
-    "SCALE_DYNAMIC", "SCALE_STATIC",
+    "SCALE_DYNAMIC", "SCALE_STATIC", "nvfp4_set_debug_checks",
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_dequantize",
     "nvfp4_fake_quantize",
     "FakeQuantizeSTE", "fake_quantize_ste",

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "nvfp4")
 LIB = os.path.join(PKG, "libnvfp4.so")
 
-SOURCES = ["quantize.hip", "dequantize.hip", "prepack.hip", "gemm.hip", "gemm_skinny.hip", "mxfp4.hip", "nvfp4_api.cpp"]
+SOURCES = ["quantize.hip", "dequantize.hip", "prepack.hip", "gemm.hip", "gemm_skinny.hip", "mxfp4.hip", "debug_check.hip", "nvfp4_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

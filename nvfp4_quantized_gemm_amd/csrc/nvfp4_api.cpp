@@ -5,8 +5,11 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 
+#include "debug_check.hpp"
 #include "launch.hpp"
 
 using namespace nvfp4;
@@ -65,6 +68,48 @@ nvfp4_status_t check_gemm_extent(int64_t M, int64_t N, int64_t K, int64_t lda) {
 
 nvfp4_status_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
+// Debug checks: -1 not yet read from NVFP4_DEBUG, 0 off, 1 on.
+std::atomic<int> debug_state{-1};
+
+bool debug_on() {
+  int d = debug_state.load(std::memory_order_acquire);
+  if (d < 0) {
+    const char *v = std::getenv("NVFP4_DEBUG");
+    int expected = -1;
+    debug_state.compare_exchange_strong(expected, (v && v[0] && std::strcmp(v, "0") != 0) ? 1 : 0,
+                                        std::memory_order_acq_rel);
+    d = debug_state.load(std::memory_order_acquire);
+  }
+  return d == 1;
+}
+
+// With debug checks on, scan the device data a call is about to read (the header lists the rules).
+nvfp4_status_t debug_scan(void *stream, std::initializer_list<DebugRegion> regions) {
+  if (!debug_on()) return NVFP4_OK;
+  bool violated = false, skipped = false;
+  if (debug_scan_regions(regions.begin(), (int)regions.size(), static_cast<hipStream_t>(stream), &violated,
+                         &skipped) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return violated ? NVFP4_ERR_PRECONDITION : NVFP4_OK;
+}
+
+// [rows][cols] fp32 or bf16 values at a pitch of ld elements
+DebugRegion finite_values(const void *p, nvfp4_dtype_t t, int64_t rows, int64_t cols, int64_t ld) {
+  return {p, t == NVFP4_F32 ? kCheckF32 : kCheckBF16, rows, cols, ld * elem_size(t)};
+}
+// [rows][cols] scale bytes at a pitch of ld bytes
+DebugRegion scale_bytes(const void *p, int kind, int64_t rows, int64_t cols, int64_t ld) {
+  return {p, kind, rows, cols, ld};
+}
+DebugRegion tensor_scale_of(const float *s, bool positive) {
+  return {s, positive ? kCheckScalePos : kCheckScale, 1, 1, 0};
+}
+// the scale-byte region of a prepacked [N][K] weight (it follows the code region)
+DebugRegion prepacked_scales(const void *b, int64_t N, int64_t K) {
+  const int64_t units = ((N + 31) / 32) * ((K + 127) / 128);
+  return {static_cast<const uint8_t *>(b) + units * 2048, kCheckE4M3, 1, units * 256, 0};
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,12 +126,19 @@ const char *nvfp4_status_string(nvfp4_status_t s) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_HIP: return "HIP runtime error";
     case NVFP4_ERR_DEVICE: return "current device is not gfx950";
+    case NVFP4_ERR_PRECONDITION: return "device data breaks a stated precondition (debug checks)";
     default: break;
   }
   return "unknown status";
 }
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+int nvfp4_set_debug_checks(int enable) {
+  const int prev = debug_on() ? 1 : 0;
+  debug_state.store(enable != 0 ? 1 : 0, std::memory_order_release);
+  return prev;
+}
 
 size_t nvfp4_quantize_workspace_bytes(int64_t M, int64_t K) {
   (void)M;
@@ -136,6 +188,9 @@ nvfp4_status_t nvfp4_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int64_t M
   }
   st = check_device();
   if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {finite_values(x, x_dtype, M, K, ld_x),
+                           tensor_scale_of(mode == NVFP4_SCALE_STATIC ? tensor_scale : nullptr, true)});
+  if (st != NVFP4_OK) return st;
   return hip_status(launch_quantize(x, (int)x_dtype, M, K, ld_x, block_size, packed, scales, tensor_scale,
                                     mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
                                     static_cast<hipStream_t>(stream)));
@@ -151,6 +206,9 @@ nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t x_dtype, int6
   if (mode == NVFP4_SCALE_DYNAMIC && nvfp4_quantize_workspace_bytes(M, K) > kQuantizeScratchBytes)
     return NVFP4_ERR_WORKSPACE;
   st = check_device();
+  if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {finite_values(x, x_dtype, M, K, ld_x),
+                           tensor_scale_of(mode == NVFP4_SCALE_STATIC ? tensor_scale : nullptr, true)});
   if (st != NVFP4_OK) return st;
   float *partial = nullptr;
   if (mode == NVFP4_SCALE_DYNAMIC) {
@@ -191,6 +249,9 @@ nvfp4_status_t nvfp4_fake_quantize_bs(const void *x, nvfp4_dtype_t x_dtype, int6
   }
   st = check_device();
   if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {finite_values(x, x_dtype, M, K, ld_x),
+                           tensor_scale_of(mode == NVFP4_SCALE_STATIC ? tensor_scale : nullptr, true)});
+  if (st != NVFP4_OK) return st;
   return hip_status(launch_fake_quantize(x, (int)x_dtype, M, K, ld_x, block_size, y, (int)y_dtype, ld_y,
                                          tensor_scale, mode == NVFP4_SCALE_DYNAMIC, static_cast<float *>(workspace),
                                          static_cast<hipStream_t>(stream)));
@@ -219,6 +280,9 @@ nvfp4_status_t nvfp4_dequantize_bs(const uint8_t *packed, const uint8_t *scales,
     return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {scale_bytes(scales, kCheckE4M3, M, K / block_size, K / block_size),
+                           tensor_scale_of(tensor_scale, false)});
+  if (st != NVFP4_OK) return st;
   return hip_status(launch_dequantize(packed, scales, tensor_scale, M, K, block_size, y, (int)y_dtype, ld_y,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -244,6 +308,8 @@ nvfp4_status_t nvfp4_prepack_weight_bs(const uint8_t *packed, const uint8_t *sca
   if (!packed || !scales || !prepacked) return NVFP4_ERR_NULL;
   if (!aligned(prepacked, 16)) return NVFP4_ERR_ALIGN;
   st = check_device();
+  if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {scale_bytes(scales, kCheckE4M3, N, K / block_size, K / block_size)});
   if (st != NVFP4_OK) return st;
   return hip_status(launch_prepack(packed, scales, N, K, block_size, prepacked, static_cast<hipStream_t>(stream)));
 }
@@ -314,6 +380,14 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
     if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
   }
   st = check_device();
+  if (st != NVFP4_OK) return st;
+  if (mode == NVFP4_W4A4)
+    st = debug_scan(stream, {scale_bytes(a_scales, kCheckE4M3, M, K / a_block_size, lda / a_block_size),
+                             tensor_scale_of(a_tensor_scale, false), prepacked_scales(b_prepacked, N, K),
+                             tensor_scale_of(b_tensor_scale, false)});
+  else
+    st = debug_scan(stream, {finite_values(a, NVFP4_BF16, M, K, lda), prepacked_scales(b_prepacked, N, K),
+                             tensor_scale_of(b_tensor_scale, false)});
   if (st != NVFP4_OK) return st;
   GemmArgs g;
   g.mode = (int)mode;
@@ -392,6 +466,16 @@ nvfp4_status_t nvfp4_gemm_requant_bs(nvfp4_mode_t mode, const void *a, const uin
   }
   st = check_device();
   if (st != NVFP4_OK) return st;
+  if (mode == NVFP4_W4A4)
+    st = debug_scan(stream, {scale_bytes(a_scales, kCheckE4M3, M, K / a_block_size, lda / a_block_size),
+                             tensor_scale_of(a_tensor_scale, false), prepacked_scales(b_prepacked, N, K),
+                             tensor_scale_of(b_tensor_scale, false), finite_values(bias, NVFP4_F32, 1, N, N),
+                             tensor_scale_of(out_tensor_scale, true)});
+  else
+    st = debug_scan(stream, {finite_values(a, NVFP4_BF16, M, K, lda), prepacked_scales(b_prepacked, N, K),
+                             tensor_scale_of(b_tensor_scale, false), finite_values(bias, NVFP4_F32, 1, N, N),
+                             tensor_scale_of(out_tensor_scale, true)});
+  if (st != NVFP4_OK) return st;
   GemmArgs g;
   g.mode = (int)mode;
   g.a = a;
@@ -450,6 +534,8 @@ nvfp4_status_t nvfp4_mx_quantize(const void *x, nvfp4_dtype_t x_dtype, int64_t M
   if (!aligned(x, 16) || ((ld_x * elem_size(x_dtype)) % 16) != 0 || !aligned(packed, 8)) return NVFP4_ERR_ALIGN;
   st = check_device();
   if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {finite_values(x, x_dtype, M, K, ld_x)});
+  if (st != NVFP4_OK) return st;
   return hip_status(launch_mx_quantize(x, (int)x_dtype, M, K, ld_x, packed, scales, static_cast<hipStream_t>(stream)));
 }
 
@@ -463,6 +549,8 @@ nvfp4_status_t nvfp4_mx_dequantize(const uint8_t *packed, const uint8_t *scales,
   if (ld_y < K) return NVFP4_ERR_STRIDE;
   if (!aligned(y, 16) || ((ld_y * elem_size(y_dtype)) % 16) != 0 || !aligned(packed, 8)) return NVFP4_ERR_ALIGN;
   st = check_device();
+  if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {scale_bytes(scales, kCheckE8M0, M, K / 32, K / 32)});
   if (st != NVFP4_OK) return st;
   return hip_status(launch_mx_dequantize(packed, scales, M, K, y, (int)y_dtype, ld_y, static_cast<hipStream_t>(stream)));
 }
@@ -483,6 +571,9 @@ nvfp4_status_t nvfp4_mx_gemm(const uint8_t *a, const uint8_t *a_scales, const ui
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) || !aligned(c, 16))
     return NVFP4_ERR_ALIGN;
   st = check_device();
+  if (st != NVFP4_OK) return st;
+  st = debug_scan(stream, {scale_bytes(a_scales, kCheckE8M0, M, K / 32, K / 32),
+                           scale_bytes(b_scales, kCheckE8M0, N, K / 32, K / 32)});
   if (st != NVFP4_OK) return st;
   return hip_status(launch_mx_gemm(a, a_scales, b, b_scales, M, N, K, c, (int)c_dtype, ldc,
                                    static_cast<hipStream_t>(stream)));

@@ -32,6 +32,16 @@ int main(void) {
   const int64_t big = (int64_t)1 << 62, huge = INT64_MAX;
   EXPECT(nvfp4_abi_version() == NVFP4_ABI_VERSION);
   for (int s = -1; s < 12; ++s) EXPECT(nvfp4_status_string((nvfp4_status_t)s) != NULL);
+  /* debug checks: the switch returns the previous setting; validation still comes first */
+  {
+    const int prev = nvfp4_set_debug_checks(1);
+    EXPECT(nvfp4_set_debug_checks(1) == 1);
+    EXPECT(nvfp4_quantize(P, NVFP4_BF16, 4, 24, 32, U8(P), U8(P), F(P), NVFP4_SCALE_DYNAMIC, P, 4096, NULL) ==
+           NVFP4_ERR_SHAPE);
+    EXPECT(device_or_hip(nvfp4_quantize(P, NVFP4_BF16, 4, 32, 32, U8(P), U8(P), F(P), NVFP4_SCALE_STATIC, NULL, 0,
+                                        NULL)));
+    EXPECT(nvfp4_set_debug_checks(prev) == 1);
+  }
 
   /* size queries at the edges */
   EXPECT(nvfp4_prepacked_bytes(huge, 16) == 0);

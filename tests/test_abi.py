@@ -38,10 +38,42 @@ def test_exports_every_header_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 2
+    assert L.nvfp4_abi_version() == 3
     for s in nv.Status:
         assert len(L.nvfp4_status_string(int(s))) > 0
     assert L.nvfp4_status_string(99) == b"unknown status"
+    assert b"precondition" in L.nvfp4_status_string(int(nv.Status.ERR_PRECONDITION))
+
+
+def test_debug_checks_toggle_and_validation_order(L):
+    """The switch returns the previous setting; with the checks on, host-side validation still
+    comes first (the scans need a device and run only after the device check)."""
+    prev = L.nvfp4_set_debug_checks(1)
+    try:
+        assert L.nvfp4_set_debug_checks(1) == 1
+        assert q(L, K=24) == nv.Status.ERR_SHAPE
+        assert q(L, x=PODD) == nv.Status.ERR_ALIGN
+        assert q(L, ws=NULL) == nv.Status.ERR_WORKSPACE
+        assert q(L) in (nv.Status.ERR_HIP, nv.Status.ERR_DEVICE)  # no GPU here: stops at the device check
+        assert L.nvfp4_set_debug_checks(0) == 1
+        assert L.nvfp4_set_debug_checks(0) == 0
+    finally:
+        L.nvfp4_set_debug_checks(prev)
+
+
+@pytest.mark.parametrize("env,expect", [(None, 0), ("0", 0), ("", 0), ("1", 1), ("yes", 1)])
+def test_debug_checks_initial_setting_from_environment(env, expect):
+    """NVFP4_DEBUG set and not "0" turns the checks on in a fresh process (read on first use)."""
+    import subprocess
+    import sys
+    code = ("import ctypes; L = ctypes.CDLL(%r); L.nvfp4_set_debug_checks.argtypes = [ctypes.c_int]; "
+            "print(L.nvfp4_set_debug_checks(0))" % nv.LIB_PATH)
+    e = {k: v for k, v in os.environ.items() if k != "NVFP4_DEBUG"}
+    if env is not None:
+        e["NVFP4_DEBUG"] = env
+    r = subprocess.run([sys.executable, "-c", code], env=e, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == str(expect)
 
 
 def test_size_queries(L):

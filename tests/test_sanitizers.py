@@ -39,7 +39,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
     assert "runtime error" not in r.stderr
 
 
-SOURCES = ["quantize.hip", "dequantize.hip", "prepack.hip", "gemm.hip", "gemm_skinny.hip", "mxfp4.hip", "nvfp4_api.cpp"]
+SOURCES = ["quantize.hip", "dequantize.hip", "prepack.hip", "gemm.hip", "gemm_skinny.hip", "mxfp4.hip", "debug_check.hip", "nvfp4_api.cpp"]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
