@@ -283,9 +283,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < TN; ++j) {
         const int unit = wn * (BN / WN / 32) + j;
         const uint32_t w = *reinterpret_cast<const uint32_t *>(st + Cfg::kALds + Cfg::kASLds + Cfg::kBLds + (unit * 64 + lane) * 4);
-        // units past N hold a clamped copy of the last unit and their results are never stored:
-        // zero scales make their operands zero, which draws less power in the matrix cores
-        Sb[j] = (n0 / 32 + unit < Nu) ? w : 0u;
+        Sb[j] = w;
       }
     };
     auto cvt_scales = [&](f16x2 (*ea)[2], f16x2 (*eb)[2]) {
@@ -296,8 +294,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        eb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[j], 1.0f, false);
-        eb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[j], 1.0f, true);
+        // units past N hold a clamped copy of the last unit and their results are never stored:
+        // zero scales make their operands zero, which draws less power in the matrix cores
+        const uint32_t sb = (n0 / 32 + wn * (BN / WN / 32) + j < Nu) ? Sb[j] : 0u;
+        eb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+        eb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, true);
       }
     };
     // stage 1: decode the codes of step s (0..7) of a chunk from part registers (ra, rb) into Q[s & 1]
