@@ -515,22 +515,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         for (int t = 0; t < 4; ++t) eb[j][t] = e4m3_to_f32((bsw[j] >> (8 * t)) & 0xffu);
       bf16x8 bf[2][TN];
       u32x4 ar[2][TM];
-      auto deq = [&](int s, int slot) {
-        const int p = s >> 2, q = s & 3, blk = s >> 1;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[slot][j] = dequant_bf16x8(bc[p][j][q], eb[j][blk]);
+      auto read_a = [&](int s, int slot) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int sub = wm * (BM / WM / 32) + i;
           ar[slot][i] = *reinterpret_cast<const u32x4 *>(sA + ((sub * 8 + s) * 64 + lane) * 16);
         }
       };
-      deq(0, 0);
+      auto deq_b = [&](int s, int slot) {
+        const int p = s >> 2, q = s & 3, blk = s >> 1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[slot][j] = dequant_bf16x8(bc[p][j][q], eb[j][blk]);
+      };
+      read_a(0, 0);
+      deq_b(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int slot = s & 1;
-        if (s + 1 < 8) deq(s + 1, slot ^ 1);
+        // The next step's A reads go out before this step's MFMAs, which hide their latency.  The
+        // wait for this step's reads (issued a step ago) is explicit and comes first: left to the
+        // compiler, the wait in front of the MFMAs would also cover the reads just issued.
+        if (s + 1 < 8) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+          read_a(s + 1, slot ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+          deq_b(s + 1, slot ^ 1);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const bf16x8 afr = __builtin_bit_cast(bf16x8, ar[slot][i]);
