@@ -260,7 +260,9 @@ nvfp4_status_t nvfp4_gemm_bs(nvfp4_mode_t mode, const void *a, const uint8_t *a_
  * All calls on one GPU share its scratch: calls that overlap on one GPU (different streams without
  * ordering between them) race and give undefined results; calls ordered on a stream do not.  No
  * scratch contents carry from one call to the next (each call writes every partial it reads).
- * STATIC mode uses no scratch.
+ * STATIC mode uses no scratch.  With debug checks on (nvfp4_set_debug_checks) the call also scans
+ * its input first and waits on its stream, as every call then does; the scans allocate nothing
+ * either (their flag words are another static device array).
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t x_dtype, int64_t M, int64_t K, int64_t ld_x,
                                       int block_size, uint8_t *packed, uint8_t *scales, float *tensor_scale,
