@@ -102,7 +102,9 @@ int nvfp4_abi_version(void);
  *                                          requantizing: bias finite, output S finite and > 0
  *   MX dequantize, MX GEMM                 E8M0 scale bytes not 0xFF
  * (unpack reads only bytes and is not scanned).  The wait makes every call synchronous.  A stream
- * under graph capture cannot be waited on, so captured calls skip the scans.  The scans use a
+ * under graph capture cannot be waited on, so captured calls skip the scans (a call on another
+ * stream while a process-wide capture is running gets the runtime's refusal of its memset or
+ * wait as NVFP4_ERR_HIP).  The scans use a
  * library-owned flag word per call in flight (64 of them, taken round-robin per device): more than
  * 64 calls scanning at once on one device may see each other's violations.
  *
