@@ -156,6 +156,31 @@ def test_gemm_checks(debug):
     rejected("W4A16 GEMM, inf activation", lambda: nv.nvfp4_gemm(nv.W4A16, xb, None, None, bp, wS, N, K, out=out), out)
 
 
+@pytest.mark.parametrize("M,K", [(8, 1024), (512, 4096)])
+def test_gemm_checks_skinny_and_split(debug, M, K):
+    """The scans stop the call before any launch path: the streaming kernel for few rows (M = 8)
+    and a K split with its fp32 partials and reduction (M = 512, K = 4096)."""
+    N = 512
+    g = torch.Generator().manual_seed(M + K)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(DEV)
+    wp, ws, wS = _weight(N, K, 15)
+    bp = nv.nvfp4_prepack_weight(wp, ws)
+    a, as_, aS = nv.nvfp4_quantize(x)
+    same_with_checks_off(f"W4A16 GEMM M={M} K={K}",
+                         lambda: [nv.nvfp4_gemm(nv.W4A16, x, None, None, bp, wS, N, K, torch.float32)])
+    same_with_checks_off(f"W4A4 GEMM M={M} K={K}",
+                         lambda: [nv.nvfp4_gemm(nv.W4A4, a, as_, aS, bp, wS, N, K, torch.float32)])
+    out = sentinel((M, N), torch.float32, 3.0)
+    xb = x.clone()
+    xb[M - 1, 0] = float("nan")
+    rejected(f"W4A16 GEMM M={M} K={K}, NaN activation",
+             lambda: nv.nvfp4_gemm(nv.W4A16, xb, None, None, bp, wS, N, K, out=out), out)
+    asb = as_.clone()
+    asb[0, K // 16 - 1] = 0x7F
+    rejected(f"W4A4 GEMM M={M} K={K}, NaN activation scale",
+             lambda: nv.nvfp4_gemm(nv.W4A4, a, asb, aS, bp, wS, N, K, out=out), out)
+
+
 def test_gemm_strided_activation_padding_not_scanned(debug):
     """W4A4 with lda > K: NaN scale bytes in the padding columns of the activation scales are not
     read by the call and do not trip the checks; one in the last column read does."""
