@@ -308,7 +308,8 @@ DOMINANT = "fc2"  # the block's longest GEMM call (4608 -> 1152)
 # --kernel-probe shapes: (mode, M, N, K); the PixArt linears use the block's own inputs
 PROBE_SHAPES = {"qkv": None, "proj": None, "fc1": None, "fc2": None,
                 "video_qkv": ("W4A4", 10240, 9216, 3072), "w4a16_up_256": ("W4A16", 256, 12288, 3072),
-                "w4a16_up_4096": ("W4A16", 4096, 12288, 3072)}
+                "w4a16_up_4096": ("W4A16", 4096, 12288, 3072),
+                "mx_qkv": ("MX", "qkv"), "mx_fc2": ("MX", "fc2"), "mx_cube": ("MX", 8192, 8192, 8192)}
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fc2_traffic.json")
 KERNEL_SOURCES = ("gemm.hip", "launch.hpp", "common.hpp", "epilogue.hpp", "quant_core.hpp")  # the dominant GEMM call's code
@@ -355,6 +356,22 @@ def kernel_probe(args, layers, gemm):
         L = next(L for L in layers if L["name"] == name)
         print(f"probe: nvfp4_gemm W4A4 {name} M={L['M']} N={L['N']} K={L['K']} x {args.steps}", flush=True)
         call = lambda: gemm(L)
+    elif PROBE_SHAPES[name][0] == "MX":
+        # MXFP4 GEMM: a PixArt linear on the block's own inputs, or a random cube
+        if len(PROBE_SHAPES[name]) == 2:
+            L = next(L for L in layers if L["name"] == PROBE_SHAPES[name][1])
+            xa, wb = L["x"], L["w_cpu"].cuda()
+        else:
+            _, M, N, K = PROBE_SHAPES[name]
+            g = torch.Generator().manual_seed(5)
+            xa = torch.randn(M, K, generator=g).to(torch.bfloat16).cuda()
+            wb = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16).cuda()
+        a, a_s = nv.nvfp4_mx_quantize(xa)
+        b, b_s = nv.nvfp4_mx_quantize(wb)
+        y = torch.empty((xa.shape[0], wb.shape[0]), dtype=torch.bfloat16, device="cuda")
+        print(f"probe: nvfp4_mx_gemm {name} M={xa.shape[0]} N={wb.shape[0]} K={xa.shape[1]} x {args.steps}",
+              flush=True)
+        call = lambda: nv.nvfp4_mx_gemm(a, a_s, b, b_s, out=y)
     else:
         mode, M, N, K = PROBE_SHAPES[name]
         g = torch.Generator().manual_seed(5)
